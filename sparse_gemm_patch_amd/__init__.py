@@ -1,0 +1,14 @@
+"""PATCH hybrid dense / 2:4 tile GEMM for MI355X (gfx950).
+
+The compute path is the C-ABI library ``libpatch.so`` (HIP kernels); this
+package is a thin ctypes binding over it.  Importing the package does not load
+the library; the first call does, and fails loudly if it is missing.
+"""
+__all__ = ["pack", "mask_unpack", "PackedWeight", "PatchError", "lib_path"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import api
+        return getattr(api, name)
+    raise AttributeError(name)
