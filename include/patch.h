@@ -1,0 +1,184 @@
+/*
+ * patch.h -- C ABI of libpatch.so: the PATCH hybrid dense / 2:4 tile GEMM on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * PATCH assigns every tile of a weight matrix to be either dense (0% sparsity)
+ * or 2:4 sparse (50%), so the global sparsity can sit anywhere between 0% and
+ * 50% ("PATCH: Learnable Tile-level Hybrid Sparsity for LLMs", Abstract).  The
+ * released artifact is a bit-packed binary keep/prune mask over frozen base
+ * weights, and applying it zeroes the pruned weights (model card
+ * "llama_3.2_1b-PATCH-45Sparse", description and "How to use").  Hardware tiles
+ * are 128x128, 128x64, 64x128 and 64x64 (same card, "Training
+ * hyper-parameters").
+ *
+ * This library takes W (bf16, nn.Linear layout [N][K]) plus such a mask,
+ * validates that every tile is dense or 2:4 along K, compresses W into a packed
+ * weight, and computes Y = X . W_masked^T with dense tiles on bf16 MFMA and 2:4
+ * tiles on the sparse MFMA (smfmac) units.
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are HIP device pointers on the current device;
+ *     "host" pointers are ordinary host memory.  Device pointers must be
+ *     16-byte aligned.
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued on
+ *     it in order; only patch_pack and patch_export block the host.
+ *   - Every call returns a patch_status.  Nothing aborts and no C++ exception
+ *     crosses the ABI.  On failure patch_last_error() returns a message (per
+ *     thread, valid until the next call on that thread).
+ *   - Only gfx950 devices are supported (PATCH_E_UNSUPPORTED otherwise).
+ */
+#ifndef PATCH_H_
+#define PATCH_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PATCH_OK = 0,
+  PATCH_E_INVALID_ARG = 1, /* null / misaligned pointer, bad enum, bad leading dimension */
+  PATCH_E_SHAPE = 2,       /* tile not in {64,128}^2, or N % TN != 0, or K % TK != 0 */
+  PATCH_E_MASK = 3,        /* some tile is neither all-dense nor exactly 2:4 along K */
+  PATCH_E_HIP = 4,         /* a HIP runtime call failed (message has hipGetErrorString) */
+  PATCH_E_NOMEM = 5,       /* device allocation failed; nothing is leaked */
+  PATCH_E_UNSUPPORTED = 6  /* device is not gfx950 */
+} patch_status;
+
+/* Bit order of the packed mask: bit i of the row-major flattened [N][K] mask is
+ * bit (7 - i%8) (MSB first, numpy.packbits default) or bit (i%8) (LSB first)
+ * of byte i/8.  1 = keep. */
+typedef enum { PATCH_BITS_MSB_FIRST = 0, PATCH_BITS_LSB_FIRST = 1 } patch_bit_order;
+
+typedef enum { PATCH_OUT_BF16 = 0, PATCH_OUT_F32 = 1 } patch_out_dtype;
+
+typedef enum { PATCH_TILE_DENSE = 0, PATCH_TILE_SPARSE24 = 1 } patch_tile_type;
+
+/* Kernel selection for patch_gemm_kernel.  AUTO picks STREAM for M <= 16 and
+ * TILED otherwise; forcing one is for tests and measurements. */
+typedef enum {
+  PATCH_KERNEL_AUTO = 0,
+  PATCH_KERNEL_TILED = 1,  /* LDS-staged MFMA tiles, for prefill-sized M */
+  PATCH_KERNEL_STREAM = 2  /* split-K weight streaming, for M <= 16 (decode) */
+} patch_kernel;
+
+typedef struct patch_weight patch_weight; /* opaque, owned by the library */
+
+typedef struct {
+  int64_t n, k;                 /* W is [n][k] */
+  int32_t tile_n, tile_k;       /* TN x TK */
+  int64_t tiles_n, tiles_k;     /* n / TN, k / TK */
+  int64_t n_dense, n_sparse;    /* D and S; D + S = tiles_n * tiles_k */
+  int64_t bytes_dense;          /* D * TN * TK * 2 */
+  int64_t bytes_sparse_vals;    /* S * TN * TK     (TK/2 bf16 per row) */
+  int64_t bytes_sparse_meta;    /* S * TN * TK / 8 (one 4-bit code per group) */
+  double sparsity;              /* 0.5 * S / (D + S): fraction of pruned weights */
+  int64_t bad_tile, bad_row, bad_group; /* first invalid group, or -1 (see patch_pack) */
+} patch_info;
+
+/*
+ * patch_pack -- validate a keep mask and compress W into a packed weight.
+ *
+ * Semantics: the mask is the bit-packed keep/prune mask of the card's
+ * description; each TN x TK tile must be dense (every aligned group of four
+ * along K keeps 4) or 2:4 (every group keeps exactly 2).  A tile's type is set
+ * by its first group; the first group (tiles in row-major order, then rows,
+ * then groups along K) whose count differs, or a first group that keeps 0, 1
+ * or 3, is reported.
+ *
+ *   w          device, bf16 [n][ldw], ldw >= k, ldw % 8 == 0.  Read only.
+ *   n, k       W shape; n % tile_n == 0, k % tile_k == 0; n, k >= 0.
+ *   mask_bits  device, ceil(n*k/8) bytes, bit order `order`.  Read only.
+ *   tile_n/k   each 64 or 128.
+ *   out        receives the new handle (NULL on any failure).
+ *   info       host, may be NULL; filled on success and on PATCH_E_MASK
+ *              (bad_tile = row-major tile index, bad_row = row inside the tile,
+ *              bad_group = group of four inside that tile row).
+ *
+ * Packed format (exported by patch_export, bit-exact):
+ *   tile_map[t]  PATCH_TILE_DENSE / PATCH_TILE_SPARSE24, t = i*tiles_k + j.
+ *   tile_slot[t] number of earlier tiles of the same type.
+ *   dense_vals   [D][TN][TK] bf16, the tile copied row-major.
+ *   sparse_vals  [S][TN][TK/2] bf16: per row, per group, the two kept values
+ *                in ascending k.
+ *   sparse_meta  [S][TN][TK/8] bytes: per group the code i0 | i1 << 2 of the
+ *                kept positions (i0 < i1), two groups per byte, even group in
+ *                the low nibble.
+ *
+ * Ownership: W and the mask may be freed once this returns; the handle owns
+ * copies of everything it needs.  Blocks the host until validation is known
+ * (one device-to-host copy).
+ */
+patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
+                        const uint8_t* mask_bits, patch_bit_order order,
+                        int32_t tile_n, int32_t tile_k, void* stream,
+                        patch_weight** out, patch_info* info);
+
+/*
+ * patch_gemm -- Y = X . W_masked^T, the linear layer over the packed weight.
+ *
+ * Y[m][n] = sum_k X[m][k] * Wm[n][k] with bf16 inputs and fp32 accumulation;
+ * Wm is W with the pruned weights zeroed (card "How to use").  Dense tiles run
+ * on bf16 MFMA, 2:4 tiles on smfmac, so only kept weights are multiplied.
+ *
+ *   x      device, bf16 [m][ldx], ldx >= k, ldx % 8 == 0.
+ *   m      >= 0 rows of X (0 is a no-op).
+ *   y      device, [m][ldy] of bf16 (round to nearest even) or fp32,
+ *          ldy >= n, ldy % 8 == 0.  Written, never read.  Must not alias x.
+ *
+ * Never allocates and never blocks the host.  At most one patch_gemm per
+ * handle may be in flight at a time (the handle's split-K workspace is
+ * shared); calls on one stream are naturally ordered.
+ */
+patch_status patch_gemm(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx,
+                        void* y, int64_t ldy, patch_out_dtype y_dtype, void* stream);
+
+/* patch_gemm with the kernel chosen by the caller.  split_k <= 0 lets the
+ * library choose; for PATCH_KERNEL_STREAM a positive value forces the number
+ * of K slices (clamped to [1, tiles along K * TK/64]).  PATCH_KERNEL_STREAM
+ * needs m <= 16. */
+patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx,
+                               void* y, int64_t ldy, patch_out_dtype y_dtype,
+                               patch_kernel kernel, int32_t split_k, void* stream);
+
+/*
+ * patch_unpack -- rebuild the masked dense weight: the card's "apply the mask"
+ * (pruned weights zeroed).  Kept weights get their bf16 bits back exactly;
+ * pruned ones get +0.0 (0x0000).
+ *
+ *   w_out  device, bf16 [n][ldw], ldw >= k, ldw % 8 == 0.  Written.
+ */
+patch_status patch_unpack(const patch_weight* w, uint16_t* w_out, int64_t ldw, void* stream);
+
+/*
+ * patch_mask_unpack -- expand `count` packed mask bits into bytes 0/1
+ * (out[i] = bit i in `order`).  Pad bits past `count` are ignored.
+ *
+ *   bits  device, ceil(count/8) bytes.   out  device, count bytes.
+ */
+patch_status patch_mask_unpack(const uint8_t* bits, int64_t count, patch_bit_order order,
+                               uint8_t* out, void* stream);
+
+/* Shape, tile counts, pool sizes and sparsity of a packed weight (host struct). */
+patch_status patch_get_info(const patch_weight* w, patch_info* info);
+
+/* Copy the packed arrays to host buffers (any may be NULL to skip).  Sizes are
+ * tiles (u8 / i32 per tile) and the byte counts of patch_info.  Blocks the host
+ * until the copies and all work queued on the handle's last stream are done. */
+patch_status patch_export(const patch_weight* w, uint8_t* tile_map, int32_t* tile_slot,
+                          uint16_t* dense_vals, uint16_t* sparse_vals, uint8_t* sparse_meta);
+
+/* Free a handle and its device memory (NULL is a no-op).  The caller must make
+ * sure no work using it is still in flight. */
+void patch_destroy(patch_weight* w);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* patch_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PATCH_H_ */

@@ -1,0 +1,367 @@
+// C ABI of libpatch.so (declared in include/patch.h): argument checks, the
+// packed-weight handle, status codes and stream-ordered kernel launches.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "patch_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+patch_status fail(patch_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+patch_status ok() {
+  g_err.clear();
+  return PATCH_OK;
+}
+
+patch_status hip_fail(hipError_t e, const char* what) {
+  return fail(PATCH_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Device allocation with a test hook: PATCH_TEST_FAIL_ALLOC=<n> makes the n-th
+// allocation (1-based) of the calling process fail, to exercise clean-up paths.
+hipError_t dev_alloc(void** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) return hipSuccess;
+  static int counter = 0;
+  const char* env = getenv("PATCH_TEST_FAIL_ALLOC");
+  if (env && *env) {
+    const int nth = atoi(env);
+    if (nth > 0 && ++counter == nth) {
+      counter = 0;
+      return hipErrorOutOfMemory;
+    }
+  }
+  return hipMalloc(p, bytes);
+}
+
+void dev_free(void* p) {
+  if (p) (void)hipFree(p);
+}
+
+// gfx950 check, cached per device ordinal.
+patch_status check_device(int* dev_out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  static int cache[64];  // 0 unknown, 1 supported, 2 unsupported
+  if (dev >= 0 && dev < 64 && cache[dev] == 1) {
+    *dev_out = dev;
+    return PATCH_OK;
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  const bool supported = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) cache[dev] = supported ? 1 : 2;
+  if (!supported) return fail(PATCH_E_UNSUPPORTED, "device %d is %s; only gfx950 is supported", dev, prop.gcnArchName);
+  *dev_out = dev;
+  return PATCH_OK;
+}
+
+patch_status check_tile(int64_t n, int64_t k, int32_t tn, int32_t tk) {
+  if ((tn != 64 && tn != 128) || (tk != 64 && tk != 128))
+    return fail(PATCH_E_SHAPE, "tile %dx%d: each side must be 64 or 128", tn, tk);
+  if (n < 0 || k < 0) return fail(PATCH_E_SHAPE, "negative shape %lldx%lld", (long long)n, (long long)k);
+  if (n % tn || k % tk)
+    return fail(PATCH_E_SHAPE, "W %lldx%lld is not a whole number of %dx%d tiles", (long long)n, (long long)k, tn,
+                tk);
+  if ((n / tn) * (k / tk) > 0x3FFFFFFF) return fail(PATCH_E_SHAPE, "too many tiles");
+  return PATCH_OK;
+}
+
+void fill_info(const patch_weight* w, patch_info* info) {
+  info->n = w->n;
+  info->k = w->k;
+  info->tile_n = w->tn;
+  info->tile_k = w->tk;
+  info->tiles_n = w->tiles_n;
+  info->tiles_k = w->tiles_k;
+  info->n_dense = w->n_dense;
+  info->n_sparse = w->n_sparse;
+  info->bytes_dense = w->n_dense * w->tn * w->tk * 2;
+  info->bytes_sparse_vals = w->n_sparse * w->tn * w->tk;
+  info->bytes_sparse_meta = w->n_sparse * w->tn * w->tk / 8;
+  info->sparsity = w->tiles ? 0.5 * (double)w->n_sparse / (double)w->tiles : 0.0;
+  info->bad_tile = info->bad_row = info->bad_group = -1;
+}
+
+void free_weight(patch_weight* w) {
+  if (!w) return;
+  dev_free(w->tile_map);
+  dev_free(w->tile_desc);
+  dev_free(w->dense_vals);
+  dev_free(w->sparse_vals);
+  dev_free(w->sparse_meta);
+  dev_free(w->ws);
+  dev_free(w->counters);
+  delete w;
+}
+
+// K slices the streaming kernel may use (sizes the per-handle workspace).
+constexpr int kMaxSplits = 32;
+
+}  // namespace
+
+extern "C" {
+
+const char* patch_last_error(void) { return g_err.c_str(); }
+
+patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, const uint8_t* mask_bits,
+                        patch_bit_order order, int32_t tile_n, int32_t tile_k, void* stream, patch_weight** out,
+                        patch_info* info) {
+  if (!out) return fail(PATCH_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (order != PATCH_BITS_MSB_FIRST && order != PATCH_BITS_LSB_FIRST)
+    return fail(PATCH_E_INVALID_ARG, "bad bit order %d", (int)order);
+  patch_status st = check_tile(n, k, tile_n, tile_k);
+  if (st != PATCH_OK) return st;
+  const int64_t tiles = (n / tile_n) * (k / tile_k);
+  if (tiles > 0) {
+    if (!w || !mask_bits) return fail(PATCH_E_INVALID_ARG, "w or mask_bits is NULL");
+    if (!aligned16(w) || !aligned16(mask_bits))
+      return fail(PATCH_E_INVALID_ARG, "w and mask_bits must be 16-byte aligned");
+    if (ldw < k || ldw % 8) return fail(PATCH_E_INVALID_ARG, "ldw %lld must be >= k and a multiple of 8", (long long)ldw);
+  }
+  int dev = 0;
+  st = check_device(&dev);
+  if (st != PATCH_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  patch_weight* pw = new (std::nothrow) patch_weight();
+  if (!pw) return fail(PATCH_E_NOMEM, "host allocation failed");
+  pw->device = dev;
+  pw->n = n;
+  pw->k = k;
+  pw->tn = tile_n;
+  pw->tk = tile_k;
+  pw->tiles_n = n / tile_n;
+  pw->tiles_k = k / tile_k;
+  pw->tiles = tiles;
+  pw->last_stream = s;
+  pw->max_splits = kMaxSplits;
+
+  if (tiles == 0) {
+    if (info) fill_info(pw, info);
+    *out = pw;
+    return ok();
+  }
+
+  // Scratch for validation: [0] first bad location, [1] dense count, [2] sparse count.
+  unsigned long long* scratch = nullptr;
+  hipError_t e;
+#define PATCH_TRY_ALLOC(ptr, bytes)                                                              \
+  do {                                                                                           \
+    e = dev_alloc(reinterpret_cast<void**>(&(ptr)), (bytes));                                    \
+    if (e != hipSuccess) {                                                                       \
+      dev_free(scratch);                                                                         \
+      free_weight(pw);                                                                           \
+      return fail(PATCH_E_NOMEM, "device allocation of %lld bytes failed: %s", (long long)(bytes), \
+                  hipGetErrorString(e));                                                         \
+    }                                                                                            \
+  } while (0)
+#define PATCH_TRY_HIP(expr, what)     \
+  do {                                \
+    e = (expr);                       \
+    if (e != hipSuccess) {            \
+      dev_free(scratch);              \
+      free_weight(pw);                \
+      return hip_fail(e, what);       \
+    }                                 \
+  } while (0)
+
+  PATCH_TRY_ALLOC(scratch, 3 * sizeof(unsigned long long));
+  PATCH_TRY_ALLOC(pw->tile_map, (size_t)tiles);
+  PATCH_TRY_ALLOC(pw->tile_desc, (size_t)tiles * sizeof(int32_t));
+
+  PATCH_TRY_HIP(launch_fill_u64(scratch, 1, PATCH_NO_ERROR_LOC, s), "fill");
+  PATCH_TRY_HIP(launch_classify(mask_bits, k, (int)order, tile_n, tile_k, pw->tiles_n, pw->tiles_k, pw->tile_map,
+                                scratch, s),
+                "classify launch");
+  PATCH_TRY_HIP(launch_slot_scan(pw->tile_map, tiles, pw->tile_desc, reinterpret_cast<long long*>(scratch + 1), s),
+                "slot scan launch");
+  unsigned long long host[3] = {0, 0, 0};
+  PATCH_TRY_HIP(hipMemcpyAsync(host, scratch, sizeof(host), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+  PATCH_TRY_HIP(hipStreamSynchronize(s), "hipStreamSynchronize");
+
+  if (host[0] != PATCH_NO_ERROR_LOC) {
+    const int64_t per_tile = (int64_t)tile_n * tile_k / 4;
+    const int64_t loc = (int64_t)host[0];
+    const int64_t bt = loc / per_tile, rem = loc % per_tile;
+    const int64_t br = rem / (tile_k / 4), bg = rem % (tile_k / 4);
+    if (info) {
+      fill_info(pw, info);
+      info->n_dense = info->n_sparse = 0;
+      info->bad_tile = bt;
+      info->bad_row = br;
+      info->bad_group = bg;
+    }
+    dev_free(scratch);
+    free_weight(pw);
+    return fail(PATCH_E_MASK,
+                "mask is not tile-wise dense / 2:4: tile %lld (tile row %lld, tile col %lld), row %lld in tile, "
+                "group %lld along K",
+                (long long)bt, (long long)(bt / (k / tile_k)), (long long)(bt % (k / tile_k)), (long long)br,
+                (long long)bg);
+  }
+  pw->n_dense = (int64_t)host[1];
+  pw->n_sparse = (int64_t)host[2];
+
+  PATCH_TRY_ALLOC(pw->dense_vals, (size_t)pw->n_dense * tile_n * tile_k * 2);
+  PATCH_TRY_ALLOC(pw->sparse_vals, (size_t)pw->n_sparse * tile_n * tile_k);
+  PATCH_TRY_ALLOC(pw->sparse_meta, (size_t)pw->n_sparse * tile_n * tile_k / 8);
+  PATCH_TRY_ALLOC(pw->ws, (size_t)kMaxSplits * 16 * n * sizeof(float));
+  PATCH_TRY_ALLOC(pw->counters, (size_t)(n / 64) * sizeof(uint32_t));
+  PATCH_TRY_HIP(launch_fill_u32(pw->counters, n / 64, 0u, s), "fill counters");
+  PATCH_TRY_HIP(launch_compress(w, ldw, mask_bits, k, (int)order, tile_n, tile_k, pw->tiles_n, pw->tiles_k,
+                                pw->tile_desc, pw->dense_vals, pw->sparse_vals, pw->sparse_meta, s),
+                "compress launch");
+  // W and the mask belong to the caller and may be released as soon as we return.
+  PATCH_TRY_HIP(hipStreamSynchronize(s), "hipStreamSynchronize");
+  dev_free(scratch);
+#undef PATCH_TRY_ALLOC
+#undef PATCH_TRY_HIP
+  if (info) fill_info(pw, info);
+  *out = pw;
+  return ok();
+}
+
+static patch_status gemm_common(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y,
+                                int64_t ldy, patch_out_dtype y_dtype, patch_kernel kernel, int32_t split_k,
+                                void* stream) {
+  if (!w) return fail(PATCH_E_INVALID_ARG, "weight handle is NULL");
+  if (y_dtype != PATCH_OUT_BF16 && y_dtype != PATCH_OUT_F32)
+    return fail(PATCH_E_INVALID_ARG, "bad output dtype %d", (int)y_dtype);
+  if (kernel != PATCH_KERNEL_AUTO && kernel != PATCH_KERNEL_TILED && kernel != PATCH_KERNEL_STREAM)
+    return fail(PATCH_E_INVALID_ARG, "bad kernel %d", (int)kernel);
+  if (m < 0) return fail(PATCH_E_INVALID_ARG, "m = %lld < 0", (long long)m);
+  if (kernel == PATCH_KERNEL_STREAM && m > 16)
+    return fail(PATCH_E_INVALID_ARG, "the streaming kernel takes m <= 16, got %lld", (long long)m);
+  if (m == 0 || w->n == 0) return ok();
+  if (!y) return fail(PATCH_E_INVALID_ARG, "y is NULL");
+  if (!aligned16(y)) return fail(PATCH_E_INVALID_ARG, "y must be 16-byte aligned");
+  if (ldy < w->n || ldy % 8) return fail(PATCH_E_INVALID_ARG, "ldy %lld must be >= n and a multiple of 8", (long long)ldy);
+  if (w->k > 0) {  // with K = 0, X is never read and Y is all zeros
+    if (!x) return fail(PATCH_E_INVALID_ARG, "x is NULL");
+    if (!aligned16(x)) return fail(PATCH_E_INVALID_ARG, "x must be 16-byte aligned");
+    if (ldx < w->k || ldx % 8) return fail(PATCH_E_INVALID_ARG, "ldx %lld must be >= k and a multiple of 8", (long long)ldx);
+  }
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != w->device) return fail(PATCH_E_INVALID_ARG, "weight lives on device %d, current device is %d", w->device, dev);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const_cast<patch_weight*>(w)->last_stream = s;
+  const int f32 = y_dtype == PATCH_OUT_F32;
+  if (w->k == 0) {
+    e = launch_fill_zero_y(y, m, w->n, ldy, f32, s);
+  } else {
+    const bool stream_kernel = kernel == PATCH_KERNEL_STREAM || (kernel == PATCH_KERNEL_AUTO && m <= 16);
+    e = stream_kernel ? launch_gemm_stream(w, x, m, ldx, y, ldy, f32, split_k, s)
+                      : launch_gemm_tiled(w, x, m, ldx, y, ldy, f32, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return ok();
+}
+
+patch_status patch_gemm(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y, int64_t ldy,
+                        patch_out_dtype y_dtype, void* stream) {
+  return gemm_common(w, x, m, ldx, y, ldy, y_dtype, PATCH_KERNEL_AUTO, 0, stream);
+}
+
+patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y,
+                               int64_t ldy, patch_out_dtype y_dtype, patch_kernel kernel, int32_t split_k,
+                               void* stream) {
+  return gemm_common(w, x, m, ldx, y, ldy, y_dtype, kernel, split_k, stream);
+}
+
+patch_status patch_unpack(const patch_weight* w, uint16_t* w_out, int64_t ldw, void* stream) {
+  if (!w) return fail(PATCH_E_INVALID_ARG, "weight handle is NULL");
+  if (w->tiles == 0) return ok();
+  if (!w_out) return fail(PATCH_E_INVALID_ARG, "w_out is NULL");
+  if (!aligned16(w_out)) return fail(PATCH_E_INVALID_ARG, "w_out must be 16-byte aligned");
+  if (ldw < w->k || ldw % 8) return fail(PATCH_E_INVALID_ARG, "ldw %lld must be >= k and a multiple of 8", (long long)ldw);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != w->device) return fail(PATCH_E_INVALID_ARG, "weight lives on device %d, current device is %d", w->device, dev);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const_cast<patch_weight*>(w)->last_stream = s;
+  e = launch_decompress(w, w_out, ldw, s);
+  if (e != hipSuccess) return hip_fail(e, "unpack launch");
+  return ok();
+}
+
+patch_status patch_mask_unpack(const uint8_t* bits, int64_t count, patch_bit_order order, uint8_t* out,
+                               void* stream) {
+  if (order != PATCH_BITS_MSB_FIRST && order != PATCH_BITS_LSB_FIRST)
+    return fail(PATCH_E_INVALID_ARG, "bad bit order %d", (int)order);
+  if (count < 0) return fail(PATCH_E_INVALID_ARG, "count < 0");
+  if (count == 0) return ok();
+  if (!bits || !out) return fail(PATCH_E_INVALID_ARG, "bits or out is NULL");
+  int dev = 0;
+  patch_status st = check_device(&dev);
+  if (st != PATCH_OK) return st;
+  hipError_t e = launch_mask_unpack(bits, count, (int)order, out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mask unpack launch");
+  return ok();
+}
+
+patch_status patch_get_info(const patch_weight* w, patch_info* info) {
+  if (!w || !info) return fail(PATCH_E_INVALID_ARG, "NULL argument");
+  fill_info(w, info);
+  return ok();
+}
+
+patch_status patch_export(const patch_weight* w, uint8_t* tile_map, int32_t* tile_slot, uint16_t* dense_vals,
+                          uint16_t* sparse_vals, uint8_t* sparse_meta) {
+  if (!w) return fail(PATCH_E_INVALID_ARG, "weight handle is NULL");
+  if (w->tiles == 0) return ok();
+  hipError_t e = hipStreamSynchronize(w->last_stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  if (tile_map) {
+    e = hipMemcpy(tile_map, w->tile_map, (size_t)w->tiles, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy tile_map");
+  }
+  if (tile_slot) {
+    e = hipMemcpy(tile_slot, w->tile_desc, (size_t)w->tiles * sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy tile_desc");
+    for (int64_t t = 0; t < w->tiles; ++t) tile_slot[t] >>= 1;  // desc = (slot << 1) | type
+  }
+  const size_t dv = (size_t)w->n_dense * w->tn * w->tk * 2, sv = (size_t)w->n_sparse * w->tn * w->tk,
+               sm = (size_t)w->n_sparse * w->tn * w->tk / 8;
+  if (dense_vals && dv) {
+    e = hipMemcpy(dense_vals, w->dense_vals, dv, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy dense_vals");
+  }
+  if (sparse_vals && sv) {
+    e = hipMemcpy(sparse_vals, w->sparse_vals, sv, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy sparse_vals");
+  }
+  if (sparse_meta && sm) {
+    e = hipMemcpy(sparse_meta, w->sparse_meta, sm, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy sparse_meta");
+  }
+  return ok();
+}
+
+void patch_destroy(patch_weight* w) { free_weight(w); }
+
+}  // extern "C"

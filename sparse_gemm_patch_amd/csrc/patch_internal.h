@@ -1,0 +1,69 @@
+// Internal declarations shared by the libpatch HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/patch.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Handle.  All pointers are device memory owned by the handle.
+struct patch_weight {
+  int device;
+  int64_t n, k;
+  int32_t tn, tk;
+  int64_t tiles_n, tiles_k, tiles, n_dense, n_sparse;
+  uint8_t* tile_map;     // [tiles]  PATCH_TILE_DENSE / PATCH_TILE_SPARSE24
+  int32_t* tile_desc;    // [tiles]  (slot << 1) | type: one load gives the tile's address
+  uint16_t* dense_vals;  // [D][TN][TK]
+  uint16_t* sparse_vals; // [S][TN][TK/2]
+  uint8_t* sparse_meta;  // [S][TN][TK/8]
+  // split-K workspace of the streaming kernel
+  float* ws;             // [max_splits][16][n] fp32 partial sums
+  uint32_t* counters;    // [n / 64] arrival counters, zero between calls
+  int32_t max_splits;
+  hipStream_t last_stream;
+};
+
+// Sentinel for "no invalid group found".
+#define PATCH_NO_ERROR_LOC 0xFFFFFFFFFFFFFFFFull
+
+// ---- pack kernels (pack.hip) ----
+// Writes tile_map and atomically lowers *err_loc to the first invalid group
+// (t * TN*TK/4 + row * TK/4 + group).  *err_loc must start at PATCH_NO_ERROR_LOC.
+hipError_t launch_classify(const uint8_t* bits, int64_t k, int order, int tn, int tk,
+                           int64_t tiles_n, int64_t tiles_k, uint8_t* tile_map,
+                           unsigned long long* err_loc, hipStream_t s);
+hipError_t launch_fill_u64(unsigned long long* p, int64_t count, unsigned long long v, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t v, hipStream_t s);
+// Exclusive per-type slot scan; counts[0] = D, counts[1] = S.
+hipError_t launch_slot_scan(const uint8_t* tile_map, int64_t tiles, int32_t* tile_desc,
+                            long long* counts, hipStream_t s);
+hipError_t launch_compress(const uint16_t* w, int64_t ldw, const uint8_t* bits, int64_t k, int order,
+                           int tn, int tk, int64_t tiles_n, int64_t tiles_k, const int32_t* tile_desc,
+                           uint16_t* dense_vals, uint16_t* sparse_vals, uint8_t* sparse_meta,
+                           hipStream_t s);
+hipError_t launch_decompress(const patch_weight* pw, uint16_t* w_out, int64_t ldw, hipStream_t s);
+hipError_t launch_mask_unpack(const uint8_t* bits, int64_t count, int order, uint8_t* out, hipStream_t s);
+
+// ---- GEMM kernels ----
+hipError_t launch_gemm_stream(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx,
+                              void* y, int64_t ldy, int out_f32, int split_k, hipStream_t s);
+hipError_t launch_gemm_tiled(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx,
+                             void* y, int64_t ldy, int out_f32, hipStream_t s);
+hipError_t launch_fill_zero_y(void* y, int64_t m, int64_t n, int64_t ldy, int out_f32, hipStream_t s);
+// Split count the streaming kernel uses when the caller does not force one.
+int stream_default_splits(const patch_weight* pw, int64_t m);
+
+// ---- device helpers ----
+// fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}

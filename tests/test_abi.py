@@ -1,0 +1,105 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/patch.h, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from sparse_gemm_patch_amd import api
+
+HEADER = os.path.join(ROOT, "include", "patch.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(patch_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.lib_path()):
+        pytest.skip("libpatch.so not built")
+    return api.load()
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(api.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_info_struct_layout_matches_header(tmp_path):
+    """ctypes' patch_info must match what a C compiler makes of include/patch.h."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f for f, _ in api.PatchInfo._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "patch.h"\nint main(void){\n'
+                   '  printf("%zu\\n", sizeof(patch_info));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(patch_info, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(api.PatchInfo)
+    assert got[1:] == [getattr(api.PatchInfo, f).offset for f in fields]
+
+
+def _pack(lib, w=1 << 20, n=128, k=128, ldw=128, bits=1 << 20, order=0, tn=64, tk=64):
+    h = ctypes.c_void_p(0xDEAD)
+    info = api.PatchInfo()
+    st = lib.patch_pack(ctypes.c_void_p(w), n, k, ldw, ctypes.c_void_p(bits), order, tn, tk, None,
+                        ctypes.byref(h), ctypes.byref(info))
+    return st, h.value
+
+
+def test_pack_argument_errors(lib):
+    # each of these is rejected before any HIP call, and *out is cleared
+    assert _pack(lib, tn=32) == (2, None)                 # tile side not 64/128
+    assert _pack(lib, tk=256) == (2, None)
+    assert _pack(lib, n=100) == (2, None)                 # ragged N
+    assert _pack(lib, k=96) == (2, None)                  # ragged K
+    assert _pack(lib, n=-64) == (2, None)
+    assert _pack(lib, order=7) == (1, None)               # bad bit order
+    assert _pack(lib, w=0) == (1, None)                   # NULL pointers
+    assert _pack(lib, bits=0) == (1, None)
+    assert _pack(lib, w=(1 << 20) + 2) == (1, None)       # misaligned
+    assert _pack(lib, ldw=120) == (1, None)               # ldw < k
+    assert _pack(lib, ldw=132) == (1, None)               # ldw not a multiple of 8
+    st = lib.patch_pack(None, 0, 0, 0, None, 0, 64, 64, None, None, None)
+    assert st == 1                                        # out == NULL
+
+
+def test_error_text_names_the_problem(lib):
+    _pack(lib, tn=32)
+    assert b"64 or 128" in lib.patch_last_error()
+    _pack(lib, n=100)
+    assert b"whole number" in lib.patch_last_error()
+
+
+def test_gemm_and_unpack_argument_errors(lib):
+    assert lib.patch_gemm(None, None, 1, 64, None, 64, 0, None) == 1
+    assert lib.patch_gemm_kernel(None, None, 1, 64, None, 64, 0, 0, 0, None) == 1
+    assert lib.patch_unpack(None, None, 64, None) == 1
+    assert lib.patch_get_info(None, None) == 1
+    assert lib.patch_export(None, None, None, None, None, None) == 1
+    assert lib.patch_mask_unpack(None, 8, 5, None, None) == 1      # bad order
+    assert lib.patch_mask_unpack(None, -1, 0, None, None) == 1     # negative count
+    assert lib.patch_mask_unpack(None, 0, 0, None, None) == 0      # empty is a no-op
+    lib.patch_destroy(None)                                        # NULL is a no-op
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(api, "_LIB", None)
+    monkeypatch.setenv("PATCH_LIB", str(tmp_path / "missing.so"))
+    with pytest.raises(api.PatchError):
+        api.load()

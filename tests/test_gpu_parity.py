@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Packing, unpacking and mask expansion must be bit-exact; Y must satisfy
+|Y - Y_ref| <= 1e-2 (1 + |Y_ref|) elementwise with no NaN/Inf, Y_ref the fp64
+oracle.  Exact closed forms (one-hot rows, all-ones) must match with zero
+tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_gemm_patch_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+TILES = [(128, 128), (128, 64), (64, 128), (64, 64)]
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def P():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_gemm_patch_amd import api
+    api.load()
+    return api
+
+
+def dev_u16(a):
+    """numpy uint16 bf16 bits -> torch bf16 on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def host_u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def y_host(y):
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def pack_problem(P, prob, order="big"):
+    bits = prob.bits if order == "big" else I.pack_mask_bits(prob.mask, "little")
+    return P.pack(dev_u16(prob.w), dev_u8(bits), tile=(prob.tn, prob.tk), bit_order=order)
+
+
+def check_packed(pw, prob):
+    ref = O.compress(prob.w, prob.mask, prob.tn, prob.tk)
+    got = pw.export()
+    assert np.array_equal(got["tile_map"], ref.tile_map)
+    assert np.array_equal(got["tile_slot"], ref.tile_slot)
+    assert np.array_equal(got["dense_vals"], ref.dense_vals)
+    assert np.array_equal(got["sparse_vals"], ref.sparse_vals)
+    assert np.array_equal(got["sparse_meta"], ref.sparse_meta)
+    return ref
+
+
+# ------------------------------------------------------------------ mask unpack
+
+@pytest.mark.parametrize("order", ["big", "little"])
+@pytest.mark.parametrize("count", [1, 7, 8, 9, 1000, 65536 + 3])
+def test_mask_unpack_bit_exact(P, order, count):
+    rng = np.random.default_rng(count)
+    bits = rng.integers(0, 256, size=(count + 7) // 8, dtype=np.uint8)
+    out = P.mask_unpack(dev_u8(bits), count, order).cpu().numpy()
+    assert np.array_equal(out, O.unpack_bits(bits, count, order))
+
+
+# ------------------------------------------------------------------ pack / unpack
+
+@pytest.mark.parametrize("tn,tk", TILES)
+@pytest.mark.parametrize("frac", [0.0, 0.3, 0.9, 1.0])
+def test_pack_bit_exact(P, tn, tk, frac):
+    prob = I.make_problem("pack", 1, 512, 768, tn, tk, frac=frac, cfg=20)
+    pw = pack_problem(P, prob)
+    ref = check_packed(pw, prob)
+    S = int(ref.tile_map.sum())
+    T = ref.tile_map.size
+    assert pw.info["n_sparse"] == S and pw.info["n_dense"] == T - S
+    assert pw.info["sparsity"] == 0.5 * S / T == O.measured_sparsity(prob.mask)
+    wm = host_u16(pw.unpack())
+    assert np.array_equal(wm, O.decompress(ref, 512, 768, tn, tk))
+    assert np.array_equal(wm, O.masked_weight(prob.w, prob.mask))
+
+
+def test_pack_lsb_first_and_strided_w(P):
+    prob = I.make_problem("lsb", 1, 256, 512, 64, 128, frac=0.5, cfg=21)
+    wide = np.zeros((256, 512 + 64), np.uint16)
+    wide[:, :512] = prob.w
+    w_dev = dev_u16(wide)[:, :512]
+    bits = I.pack_mask_bits(prob.mask, "little")
+    pw = P.pack(w_dev, dev_u8(bits), tile=(64, 128), bit_order="little")
+    check_packed(pw, prob)
+    out = torch.zeros((256, 512 + 128), dtype=torch.bfloat16, device="cuda")
+    pw.unpack(out=out[:, :512])
+    got = host_u16(out)
+    assert np.array_equal(got[:, :512], O.masked_weight(prob.w, prob.mask))
+    assert np.all(got[:, 512:] == 0)  # columns past K untouched
+
+
+@pytest.mark.parametrize("tn,tk", TILES)
+def test_invalid_mask_located_like_the_oracle(P, tn, tk):
+    prob = I.make_problem("bad", 1, 256, 512, tn, tk, frac=0.6, cfg=22)
+    rng = np.random.default_rng(5)
+    cases = [(int(rng.integers(0, 256)), int(rng.integers(0, 512))) for _ in range(6)] + [(255, 511), (0, 0)]
+    for r, c in cases:
+        m = prob.mask.copy()
+        m[r, c] ^= 1
+        with pytest.raises(O.MaskError) as want:
+            O.classify(m, tn, tk)
+        with pytest.raises(P.PatchError) as got:
+            P.pack(dev_u16(prob.w), dev_u8(I.pack_mask_bits(m)), tile=(tn, tk))
+        assert got.value.status_name == "PATCH_E_MASK"
+        gi = got.value.info
+        assert (gi["bad_tile"], gi["bad_row"], gi["bad_group"]) == (want.value.tile, want.value.row, want.value.group)
+
+
+def test_two_errors_report_the_first(P):
+    prob = I.make_problem("bad2", 1, 256, 256, 64, 64, frac=0.5, cfg=23)
+    m = prob.mask.copy()
+    m[200, 250] ^= 1
+    m[70, 3] ^= 1
+    with pytest.raises(O.MaskError) as want:
+        O.classify(m, 64, 64)
+    with pytest.raises(P.PatchError) as got:
+        P.pack(dev_u16(prob.w), dev_u8(I.pack_mask_bits(m)), tile=(64, 64))
+    gi = got.value.info
+    assert (gi["bad_tile"], gi["bad_row"], gi["bad_group"]) == (want.value.tile, want.value.row, want.value.group)
+
+
+def test_shape_and_argument_errors(P):
+    w = torch.zeros((192, 128), dtype=torch.bfloat16, device="cuda")
+    bits = torch.zeros(192 * 128 // 8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(P.PatchError) as e:
+        P.pack(w, bits, tile=(128, 128))
+    assert e.value.status_name == "PATCH_E_SHAPE"
+    with pytest.raises(P.PatchError) as e:
+        P.pack(w, bits, tile=(64, 32))
+    assert e.value.status_name == "PATCH_E_SHAPE"
+
+
+def test_allocation_failure_is_clean(P, monkeypatch):
+    prob = I.make_problem("nomem", 1, 256, 256, 64, 64, frac=0.5, cfg=24)
+    w, bits = dev_u16(prob.w), dev_u8(prob.bits)
+    for nth in (1, 2, 3, 4, 6, 8):
+        monkeypatch.setenv("PATCH_TEST_FAIL_ALLOC", str(nth))
+        with pytest.raises(P.PatchError) as e:
+            P.pack(w, bits, tile=(64, 64))
+        assert e.value.status_name == "PATCH_E_NOMEM"
+    monkeypatch.delenv("PATCH_TEST_FAIL_ALLOC")
+    check_packed(P.pack(w, bits, tile=(64, 64)), prob)
+
+
+def test_empty_weights(P):
+    for n, k in [(0, 128), (128, 0)]:
+        w = torch.zeros((n, k), dtype=torch.bfloat16, device="cuda")
+        bits = torch.zeros(max(1, n * k // 8), dtype=torch.uint8, device="cuda")
+        pw = P.pack(w, bits, tile=(64, 64))
+        assert pw.info["n_dense"] == pw.info["n_sparse"] == 0
+        x = torch.randn((5, k), device="cuda").to(torch.bfloat16)
+        y = pw.gemm(x, out_dtype=torch.float32)
+        assert tuple(y.shape) == (5, n) and (n == 0 or bool(torch.all(y == 0)))
+
+
+# ------------------------------------------------------------------ GEMM parity
+
+def gemm_case(P, prob, kernel="auto", out_dtype=torch.bfloat16, split_k=0):
+    pw = pack_problem(P, prob)
+    y = pw.gemm(dev_u16(prob.x), out_dtype=out_dtype, kernel=kernel, split_k=split_k)
+    torch.cuda.synchronize()
+    wm = O.masked_weight(prob.w, prob.mask)
+    ref = O.gemm_ref(prob.x, wm)
+    return y_host(y), ref
+
+
+def test_tiny_config(P):
+    """W 256x256, 128x128 tiles, 2 dense + 2 2:4 tiles chosen by seed, X 16x256."""
+    prob = I.make_problem("tiny", 16, 256, 256, 128, 128, n_sparse=2, cfg=0)
+    for kernel in ("auto", "stream", "tiled"):
+        for dt in (torch.bfloat16, torch.float32):
+            y, ref = gemm_case(P, prob, kernel, dt)
+            assert O.rel_error(y, ref) <= TOL, (kernel, dt)
+
+
+@pytest.mark.parametrize("tn,tk", TILES)
+@pytest.mark.parametrize("m", [1, 8, 16, 17, 130, 300])
+@pytest.mark.parametrize("frac", [0.0, 0.5, 1.0])
+def test_gemm_matches_oracle(P, tn, tk, m, frac):
+    prob = I.make_problem("g", m, 384, 640, tn, tk, frac=frac, cfg=30 + m)
+    for dt in (torch.bfloat16, torch.float32):
+        y, ref = gemm_case(P, prob, "auto", dt)
+        err = O.rel_error(y, ref)
+        assert err <= TOL, (dt, err)
+        if dt == torch.float32:
+            assert err <= 1e-4, err  # fp32 output: only accumulation-order error
+
+
+@pytest.mark.parametrize("kernel", ["stream", "tiled"])
+def test_one_hot_rows_exact(P, kernel):
+    prob = I.make_problem("oh", 16, 256, 512, 64, 128, frac=0.7, cfg=40)
+    ks = (np.arange(16) * 31 + 5) % 512
+    x = np.zeros((16, 512), np.uint16)
+    x[np.arange(16), ks] = 0x3F80
+    pw = pack_problem(P, prob)
+    y = pw.gemm(dev_u16(x), kernel=kernel)
+    wm = O.masked_weight(prob.w, prob.mask)
+    assert np.array_equal(host_u16(y), wm[:, ks].T)  # bf16 bits, zero tolerance
+
+
+@pytest.mark.parametrize("kernel,m", [("stream", 16), ("tiled", 200)])
+def test_ones_count_kept_exactly(P, kernel, m):
+    prob = I.make_problem("ones", m, 256, 1024, 128, 64, frac=0.6, cfg=41)
+    w1 = np.full_like(prob.w, 0x3F80)
+    pw = P.pack(dev_u16(w1), dev_u8(prob.bits), tile=(128, 64))
+    y = pw.gemm(dev_u16(np.full((m, 1024), 0x3F80, np.uint16)), out_dtype=torch.float32, kernel=kernel)
+    want = prob.mask.sum(axis=1).astype(np.float64)
+    assert np.array_equal(y_host(y), np.broadcast_to(want, (m, 256)))
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 3, 5, 8, 32])
+def test_stream_split_k_and_determinism(P, split_k):
+    prob = I.make_problem("sk", 16, 512, 2048, 128, 128, frac=0.5, cfg=42)
+    pw = pack_problem(P, prob)
+    x = dev_u16(prob.x)
+    y1 = pw.gemm(x, out_dtype=torch.float32, kernel="stream", split_k=split_k)
+    y2 = pw.gemm(x, out_dtype=torch.float32, kernel="stream", split_k=split_k)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)  # bitwise run-to-run
+    ref = O.gemm_ref(prob.x, O.masked_weight(prob.w, prob.mask))
+    assert O.rel_error(y_host(y1), ref) <= TOL
+
+
+def test_strided_x_and_y(P):
+    prob = I.make_problem("ld", 40, 256, 512, 64, 64, frac=0.5, cfg=43)
+    pw = pack_problem(P, prob)
+    xw = torch.zeros((40, 512 + 64), dtype=torch.bfloat16, device="cuda")
+    xw[:, :512] = dev_u16(prob.x)
+    yw = torch.full((40, 256 + 8), 7.0, dtype=torch.float32, device="cuda")
+    pw.gemm(xw[:, :512], out=yw[:, :256], out_dtype=torch.float32)
+    got = y_host(yw)
+    ref = O.gemm_ref(prob.x, O.masked_weight(prob.w, prob.mask))
+    assert O.rel_error(got[:, :256], ref) <= TOL
+    assert np.all(got[:, 256:] == 7.0)  # padding columns untouched
+
+
+def test_gemm_m_zero_is_noop(P):
+    prob = I.make_problem("m0", 1, 128, 128, 64, 64, frac=0.5, cfg=44)
+    pw = pack_problem(P, prob)
+    x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    assert tuple(pw.gemm(x).shape) == (0, 128)
