@@ -26,10 +26,6 @@ COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
-    # keep MFMA accumulators in VGPRs: smfmac ties its accumulator to its destination,
-    # and letting dense MFMAs use AGPRs instead makes the compiler copy accumulators
-    # between the two register files wherever dense and 2:4 code paths meet
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -7,6 +7,7 @@
 
 #include <new>
 #include <string>
+#include <vector>
 
 #include "patch_internal.h"
 
@@ -345,19 +346,47 @@ patch_status patch_export(const patch_weight* w, uint8_t* tile_map, int32_t* til
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy tile_desc");
     for (int64_t t = 0; t < w->tiles; ++t) tile_slot[t] >>= 1;  // desc = (slot << 1) | type
   }
-  const size_t dv = (size_t)w->n_dense * w->tn * w->tk * 2, sv = (size_t)w->n_sparse * w->tn * w->tk,
-               sm = (size_t)w->n_sparse * w->tn * w->tk / 8;
+  const int64_t tn = w->tn, tk = w->tk, bt = tn / 16;
+  const size_t dv = (size_t)w->n_dense * tn * tk * 2, sv = (size_t)w->n_sparse * tn * tk,
+               sm = (size_t)w->n_sparse * tn * tk / 8;
+  // The device pools are in operand order (pack.hip); convert to the row-major
+  // format of the header.  Unit u = step * TN/16 + block; lane = 16 q + r.
   if (dense_vals && dv) {
-    e = hipMemcpy(dense_vals, w->dense_vals, dv, hipMemcpyDeviceToHost);
+    std::vector<uint16_t> tmp(dv / 2);
+    e = hipMemcpy(tmp.data(), w->dense_vals, dv, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy dense_vals");
+    for (int64_t s = 0; s < w->n_dense; ++s)
+      for (int64_t row = 0; row < tn; ++row)
+        for (int64_t col = 0; col < tk; ++col) {
+          const int64_t step = col / 64, cc = col % 64, q = cc / 16, within = cc % 16;
+          const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16, dw = within / 2;
+          const int64_t src = s * tn * tk + u * 1024 + (dw & 1) * 512 + lane * 8 + (dw >> 1) * 2 + (within & 1);
+          dense_vals[(s * tn + row) * tk + col] = tmp[src];
+        }
   }
   if (sparse_vals && sv) {
-    e = hipMemcpy(sparse_vals, w->sparse_vals, sv, hipMemcpyDeviceToHost);
+    std::vector<uint16_t> tmp(sv / 2);
+    e = hipMemcpy(tmp.data(), w->sparse_vals, sv, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy sparse_vals");
+    for (int64_t s = 0; s < w->n_sparse; ++s)
+      for (int64_t row = 0; row < tn; ++row)
+        for (int64_t c = 0; c < tk / 2; ++c) {
+          const int64_t step = c / 32, q = (c % 32) / 8, j = c % 8;
+          const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16;
+          sparse_vals[(s * tn + row) * (tk / 2) + c] = tmp[s * tn * tk / 2 + u * 512 + lane * 8 + j];
+        }
   }
   if (sparse_meta && sm) {
-    e = hipMemcpy(sparse_meta, w->sparse_meta, sm, hipMemcpyDeviceToHost);
+    std::vector<uint8_t> tmp(sm);
+    e = hipMemcpy(tmp.data(), w->sparse_meta, sm, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy sparse_meta");
+    for (int64_t s = 0; s < w->n_sparse; ++s)
+      for (int64_t row = 0; row < tn; ++row)
+        for (int64_t b = 0; b < tk / 8; ++b) {
+          const int64_t step = b / 8, bb = b % 8, q = bb / 2;
+          const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16;
+          sparse_meta[(s * tn + row) * (tk / 8) + b] = tmp[s * tn * tk / 8 + u * 128 + lane * 2 + (bb & 1)];
+        }
   }
   return ok();
 }

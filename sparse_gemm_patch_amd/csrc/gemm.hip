@@ -2,23 +2,22 @@
 //
 // Every TN x TK tile of W is dense or 2:4 along K ("PATCH: Learnable
 // Tile-level Hybrid Sparsity for LLMs", Abstract; tile sizes from model card
-// "llama_3.2_1b-PATCH-45Sparse", "Training hyper-parameters").  W is the MFMA
-// "A" operand, because the gfx950 sparse MFMA (smfmac) takes its 2:4 operand
-// there; X rows are the "B" operand; each wave accumulates a block of Y^T in
-// fp32 and the epilogue writes Y[m][n].
+// "llama_3.2_1b-PATCH-45Sparse", "Training hyper-parameters").  W is the A
+// operand of smfmac 16x16x64 (the gfx950 sparse MFMA takes its 2:4 operand
+// there); X rows are the B operand; each wave accumulates blocks of Y^T in fp32
+// and the epilogue writes Y[m][n].
 //
-// gfx950 operand layouts used here (lane l, register j; R = 16 or 32 rows):
-//   dense  16x16x32 / 32x32x16 bf16: A[l%R][8*(l/R)+j], B[8*(l/R)+j][l%R]
-//   smfmac 16x16x64 / 32x32x32 bf16: compressed A row l%R holds the kept
-//          values of dense k = 16*(l/R) .. +15 (8 values, 2 per group of four);
-//          the 2-bit position of value j is bits [2j+1:2j] of the index VGPR;
-//          B register j holds k = 8*(l/R)+j (j < 8) or KK/2 + 8*(l/R)+j-8.
-//   C: 16x16 -> row 4*(l/16)+r, col l%16;  32x32 -> row 8*(r/4)+4*(l/32)+r%4, col l%32.
-// So a K chunk of X loaded as two 16-byte pieces (k = 8q.. and KK/2 + 8q..)
-// feeds both the pair of dense MFMAs and the single smfmac over that chunk,
-// and the packed 2:4 format (two kept values per group in ascending k, code
-// i0 | i1 << 2 with the even group in the low nibble) is exactly the smfmac
-// operand: 16 contiguous bytes of values plus one little-endian u16 of codes.
+// smfmac 16x16x64 bf16 on gfx950 (lane l = 16 q + r, register j):
+//   A: row r, the 8 kept values of dense k = 16 q .. 16 q + 15 (two per group of
+//      four); the 2-bit position of value j is bits [2j+1:2j] of the index VGPR
+//   B: column r, k = 8 q + j (j < 8) and 32 + 8 q + j - 8 (j >= 8)
+//   C: row 4 q + i (i = 0..3), column r
+// smfmac issues at twice the dense MFMA rate, so a dense 64-wide K step is run
+// as two smfmacs, fed kept positions (0,1) and (2,3) of every group of four
+// with the constant index words 0x4444 and 0xEEEE; that costs what the dense
+// MFMAs over the same K cost, and one instruction serves both tile types.
+// The packed pools are stored in this operand order (see pack.hip), so a
+// lane's A operand is one 16-byte load and a wave's is 1 KiB contiguous.
 #include "patch_internal.h"
 
 namespace {
@@ -95,42 +94,41 @@ __global__ __launch_bounds__(256) void k_gemm_stream(
 #pragma unroll
   for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const int bt = tn >> 4;                  // 16-row blocks per tile
+  const int blk0 = row0 >> 4;              // this row block's first 16-row block in its tile
   for (int64_t c = c_begin + wave; c < c_end; c += 4) {
     const int64_t k0 = c << 6;
     const bf16x8 xb0 = m_ok ? ld8(xrow + k0 + 8 * q) : zero8();
     const bf16x8 xb1 = m_ok ? ld8(xrow + k0 + 32 + 8 * q) : zero8();
+    const bf16x16 xb = cat16(xb0, xb1);
     const int32_t d = tile_desc[tile_row_base + (c >> ks)];
     const int64_t slot = d >> 1;
-    const int kin = (int)(c & ks) << 6;
+    const int u0 = (int)(c & ks) * bt + blk0;  // operand unit of row block b is u0 + b
     if ((d & 1) == PATCH_TILE_DENSE) {
-      const uint16_t* wt = dense_vals + slot * tn * tk + kin + 8 * q;
+      const uint8_t* wt = reinterpret_cast<const uint8_t*>(dense_vals) + (slot * tn * tk + (int64_t)u0 * 1024) * 2 + lane * 16;
       bf16x8 a0[4], a1[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const uint16_t* p = wt + (int64_t)(row0 + 16 * b + r16) * tk;
-        a0[b] = ld8(p);
-        a1[b] = ld8(p + 32);
+        a0[b] = *reinterpret_cast<const bf16x8*>(wt + b * 2048);
+        a1[b] = *reinterpret_cast<const bf16x8*>(wt + b * 2048 + 1024);
       }
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[b], xb0, acc[b], 0, 0, 0);
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[b], xb1, acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[b], xb, acc[b], 0x4444, 0, 0);
+        acc[b] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a1[b], xb, acc[b], 0xEEEE, 0, 0);
       }
     } else {
-      const uint16_t* vt = sparse_vals + slot * tn * (tk >> 1) + (kin >> 1) + 8 * q;
-      const uint8_t* mt = sparse_meta + slot * tn * (tk >> 3) + (kin >> 3) + 2 * q;
+      const uint8_t* vt = reinterpret_cast<const uint8_t*>(sparse_vals) + slot * tn * tk + (int64_t)u0 * 1024 + lane * 16;
+      const uint8_t* mt = sparse_meta + slot * tn * (tk >> 3) + (int64_t)u0 * 128 + lane * 2;
       bf16x8 a[4];
       int idx[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int row = row0 + 16 * b + r16;
-        a[b] = ld8(vt + (int64_t)row * (tk >> 1));
-        idx[b] = *reinterpret_cast<const uint16_t*>(mt + (int64_t)row * (tk >> 3));
+        a[b] = *reinterpret_cast<const bf16x8*>(vt + b * 1024);
+        idx[b] = *reinterpret_cast<const uint16_t*>(mt + b * 128);
       }
-      const bf16x16 xb = cat16(xb0, xb1);
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        acc[b] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[b], xb, acc[b], idx[b], 0, 0);
+      for (int b = 0; b < 4; ++b) acc[b] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[b], xb, acc[b], idx[b], 0, 0);
     }
   }
 
@@ -188,72 +186,69 @@ __global__ __launch_bounds__(256) void k_gemm_stream(
 // ------------------------------------------------------------------------
 // Tiled kernel for prefill-sized M.
 //
-// Workgroup = 6 waves: 4 consumers (MFMA) and 2 producers (global -> LDS).
-// The block of Y^T is 256 W rows (n) x 128 X rows (m); consumer wave w owns the
-// 64 W rows of group w and all 128 columns, as 4 x 8 blocks of 16 x 16
-// (128 fp32 accumulators per lane).  K advances 64 at a time; a 64-wide K step
-// never crosses a tile and a 64-row group never crosses a tile row, so a
-// consumer meets one tile type per step.
+// Workgroup = 8 waves in a 2 x 4 grid; the block of Y^T is 256 W rows (n) x
+// 256 X rows (m).  Wave (wn, wm) owns W rows 128 wn .. +127 (8 row blocks of
+// 16, in two 64-row groups that each lie in one tile row) and X rows
+// 64 wm .. +63 (4 column blocks): 8 x 4 accumulator blocks of 16 x 16, 128
+// fp32 accumulators per lane, two waves per SIMD.  K advances 64 at a time; a
+// step never crosses a tile.
 //
-// Everything runs on smfmac 16x16x64, which issues at twice the dense MFMA
-// rate: a 2:4 step is one smfmac per block with the stored 2-bit codes; a dense
-// step is two, fed kept positions (0,1) and (2,3) of every group of four with
-// constant codes 0x4444 and 0xEEEE.  Two of them cost what dense MFMAs over the
-// same K cost, and every accumulator update is the same instruction.
+// What bounds this kernel on MI355X is how fast a CU can pull operands out of
+// L2 (about 130 GB/s per CU, reached only when several waves issue loads).  A
+// 256 x 256 block needs 50 KiB (2:4) to 64 KiB (dense) per step for 8.4
+// dense-equivalent MFLOP, which keeps the sparse MFMA rate within reach.
 //
-// LDS holds a ring of 3 stages of 48 KiB:
-//   X:  128 rows x 128 B; 16-byte chunk c of row r at position c ^ h(r),
-//       h(r) = (r & 7) ^ ((r >> 3) & 1)
-//   W:  four 64-row groups of 8 KiB, each in its tile's own format:
-//       dense  64 rows x 128 B, chunk c at c ^ h(r)
-//       2:4    64 rows x 64 B of kept values, chunk c at c ^ (((r >> 1) ^ (r >> 3)) & 3),
-//              then 64 rows x 8 B of 2-bit codes at +4 KiB
-// The swizzles keep the 16-byte reads of 16 consecutive lanes (16 consecutive
-// rows, one logical chunk) on distinct banks whether the LDS serves 128 or
-// 256 bytes per clock.
-//
-// Producers load with global_load_lds_dwordx4 (lane i of a wave writes bytes
-// 16 i .. 16 i + 15 of a 1 KiB LDS block, so a lane fetches the global chunk
-// that belongs at its LDS position; 8 lanes still cover one 128-byte row
-// segment).  Producer p loads the steps with parity p, two steps ahead, and
-// waits for its own loads only before the barrier at which they are consumed.
-// Consumers issue no global->LDS loads, so none of their LDS reads waits on one.
-// Every wave passes exactly one barrier per step.
+// LDS holds two stages of 64 KiB:
+//   X  256 rows x 128 B; 16-byte chunk c of row r at position c ^ h(r),
+//      h(r) = (r & 7) ^ ((r >> 3) & 1), so the 16-byte reads of 16 consecutive
+//      lanes (16 rows, one chunk) fall on distinct banks.
+//   W  four 64-row groups of 8 KiB.  A group's operands for one step are
+//      contiguous in the operand-order pools and are copied verbatim: dense 4
+//      blocks x [a0 | a1] x 1 KiB; 2:4 4 blocks x 1 KiB of values, then 4 x
+//      128 B of codes at +4 KiB.  Lane l reads bytes 16 l .. 16 l + 15 of a
+//      block, which no bank conflict can touch.
+// Every wave copies its share of each step (32 X rows and a quarter of the W
+// data, always 8 copy instructions) straight from global memory into LDS with
+// global_load_lds, one step ahead, then waits for its own copies before the
+// step's barrier.  The copies are issued from inline assembly (which saves and
+// restores M0, the LDS address register): the compiler cannot tell that they
+// target the other stage, and as builtins every LDS read after them would wait
+// for them to land.  The kernel issues no other vector-memory loads, so the
+// explicit waits are the only ones these copies need.
 // ------------------------------------------------------------------------
 namespace tiled {
-constexpr int BN = 256, BM = 128, BK = 64;
-constexpr int X_BYTES = BM * 128;          // 16 KiB
+constexpr int BN = 256, BM = 256, BK = 64;
+constexpr int X_BYTES = BM * 128;          // 32 KiB
 constexpr int G_BYTES = 64 * 128;          // 8 KiB per 64-row W group
 constexpr int STAGE_BYTES = X_BYTES + 4 * G_BYTES;
-constexpr int STAGES = 3;
-constexpr int CONSUMERS = 4, PRODUCERS = 2;
-constexpr int GROUP_N = 4;  // block columns per group of the block order
-constexpr int THREADS = 64 * (CONSUMERS + PRODUCERS);
+constexpr int STAGES = 2;
+constexpr int GROUP_N = 4;                 // block columns per group of the block order
 }  // namespace tiled
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void g2l16(const void* src, uint8_t* lds_block) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 0);
+// global -> LDS copy of 16 (or 4) bytes per lane; lane i writes LDS bytes
+// lds_addr + 16 i (4 i).  lds_addr must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(src) : "memory");
 }
-__device__ __forceinline__ void g2l4(const void* src, uint8_t* lds_block) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 4, 0, 0);
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(src) : "memory");
+}
+// Wait for this wave's copies and LDS reads, then synchronise the workgroup.
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 __device__ __forceinline__ bf16x8 lds8(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
-// Workgroup barrier without the implied memory fences: the producers wait for
-// their own loads explicitly, and the "memory" clobber keeps the compiler from
-// moving LDS accesses across it.
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Output block of this workgroup.  The dispatcher deals workgroup i to XCD
 // i % 8; renumbering so that each XCD owns a contiguous range of blocks, walked
 // in groups of GROUP_N block columns (m fastest inside a group), makes the
-// ~32 workgroups resident on one XCD cover about 4 x 8 blocks and share their W
-// and X slabs in that XCD's L2.
+// workgroups resident on one XCD cover a compact region and share their W and
+// X in that XCD's L2.
 __device__ __forceinline__ void block_origin(int64_t n, int64_t m, int64_t& n0, int64_t& m0) {
   using namespace tiled;
   const int nbn = (int)((n + BN - 1) / BN), nbm = (int)((m + BM - 1) / BM);
@@ -270,161 +265,164 @@ __device__ __forceinline__ void block_origin(int64_t n, int64_t m, int64_t& n0, 
 }
 
 template <bool F32>
-__global__ __launch_bounds__(tiled::THREADS, 1) void k_gemm_tiled(
+__global__ __launch_bounds__(512, 1) void k_gemm_tiled(
     const int32_t* __restrict__ tile_desc, const uint16_t* __restrict__ dense_vals,
     const uint16_t* __restrict__ sparse_vals, const uint8_t* __restrict__ sparse_meta, int tn, int tk,
     int64_t tiles_k, int64_t n, int64_t k, const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
     void* __restrict__ y, int64_t ldy) {
   using namespace tiled;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave >> 2, wm = wave & 3;
+  const int q = lane >> 4, r16 = lane & 15;
   int64_t n0, m0;
   block_origin(n, m, n0, m0);
   const int nsteps = (int)(k / BK);
   const int ks = tk == 128;           // 64-wide K steps per tile column: 1 << ks
   const int ns = tn == 128 ? 7 : 6;   // log2(TN)
+  const int bt = tn >> 4;             // 16-row blocks per tile
 
-  if (wave >= CONSUMERS) {
-    // ------------------------------ producer ------------------------------
-    // Per-lane byte offsets are fixed for the whole K loop; each step only moves
-    // the uniform base pointers (tile slot and K position), so every load is a
-    // scalar-base + 32-bit-offset global_load_lds with no per-step vector math.
-    const int p = wave - CONSUMERS;
-    const int lrow8 = lane >> 3;   // row within a 1 KiB block of 128-byte rows
-    const int lpos8 = lane & 7;    // 16-byte position within the row
-    uint32_t xoff[BM / 8];
+  // ---- copy roles: X rows 32 wave + 8 j + (lane >> 3), logical chunk (lane & 7) ^ h(row)
+  // (rows past M clamp to M - 1: they only feed Y rows that are never stored),
+  // and half (wave & 1) of W group wave >> 1 (rows n0 + 64 (wave >> 1) .. +63).
+  const uint16_t* xp[4];
 #pragma unroll
-    for (int j = 0; j < BM / 8; ++j) {
-      const int row = 8 * j + lrow8;
-      int64_t gm = m0 + row;
-      if (gm > m - 1) gm = m - 1;  // rows past M only feed Y rows that are never stored
-      xoff[j] = (uint32_t)((gm - m0) * ldx * 2) + 16u * (uint32_t)(lpos8 ^ swz8(row));
+  for (int j = 0; j < 4; ++j) {
+    const int row = 32 * wave + 8 * j + (lane >> 3);
+    int64_t gm = m0 + row;
+    if (gm > m - 1) gm = m - 1;
+    xp[j] = x + gm * ldx + 8 * ((lane & 7) ^ swz8(row));
+  }
+  const int cg = wave >> 1, chalf = wave & 1;  // copied group and half of its copies
+  const int64_t gn0 = n0 + 64 * cg;
+  const bool g_ok = gn0 < n;
+  const int64_t g_desc = (gn0 >> ns) * tiles_k;
+  const int g_blk = (int)((gn0 & (tn - 1)) >> 4);
+  const uint8_t* dsrc = reinterpret_cast<const uint8_t*>(dense_vals) + lane * 16;
+  const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(sparse_vals) + lane * 16;
+  const uint8_t* msrc = sparse_meta + lane * 4;
+
+  // 8 copies per wave and step, whatever the tile types, so that the waits
+  // before each barrier are the same.  A group's 8 KiB: dense = 8 blocks of
+  // 1 KiB (half h copies blocks 4 h .. 4 h + 3); 2:4 = 4 value blocks (half 0)
+  // and 512 B of codes (half 1: two 256 B copies, each issued twice).
+  auto issue = [&](int step, int stage) {
+    const uint32_t st = lds_base + stage * STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(xp[j] + step * 64, st + (32 * wave + 8 * j) * 128);
+    const uint32_t g = st + X_BYTES + cg * G_BYTES;
+    if (!g_ok) {  // group past N: keep the count with harmless copies into its unused slot
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(xp[j] + step * 64, g + 1024 * (4 * chalf + j));
+      return;
     }
-    uint32_t doff[8], soff[4], moff[2];
+    const int32_t d = tile_desc[g_desc + (step >> ks)];
+    const int64_t slot = d >> 1;
+    const int64_t u0 = (step & ks) * bt + g_blk;  // first operand unit of the group
+    if ((d & 1) == PATCH_TILE_DENSE) {
+      const uint8_t* src = dsrc + (slot * tn * tk + u0 * 1024) * 2;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = 8 * j + lrow8;
-      doff[j] = 2u * (uint32_t)(row * tk + 8 * (lpos8 ^ swz8(row)));
+      for (int j = 4 * chalf; j < 4 * chalf + 4; ++j) dma16(src + 1024 * j, g + 1024 * j);
+    } else if (chalf == 0) {
+      const uint8_t* src = ssrc + slot * tn * tk + u0 * 1024;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(src + 1024 * j, g + 1024 * j);
+    } else {
+      const uint8_t* mp = msrc + slot * tn * (tk >> 3) + u0 * 128;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma4(mp + 256 * (j & 1), g + 4096 + 256 * (j & 1));
     }
+  };
+
+  // ---- compute role: W rows 128 wn .. +127 (groups 2 wn, 2 wn + 1), X rows 64 wm .. +63
+  const int64_t wrow0 = n0 + 128 * wn;
+  const bool hok0 = wrow0 < n, hok1 = wrow0 + 64 < n;
+  const int64_t hdesc0 = (wrow0 >> ns) * tiles_k, hdesc1 = ((wrow0 + 64) >> ns) * tiles_k;
+
+  f32x4 acc[8][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // 16 rows of 64 bytes per 1 KiB block
-      const int row = 16 * j + (lane >> 2);
-      soff[j] = 2u * (uint32_t)(row * (tk >> 1) + 8 * ((lane & 3) ^ swz4(row)));
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int step, int stage) {
+    const uint8_t* cur = lds + stage * STAGE_BYTES;
+    const int d0 = hok0 ? ((tile_desc[hdesc0 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
+    const int d1 = hok1 ? ((tile_desc[hdesc1 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
+    bf16x16 b[4];
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm) {
+      const int r = 64 * wm + 16 * bm + r16;
+      b[bm] = cat16(lds8(cur + r * 128 + ((q ^ swz8(r)) << 4)), lds8(cur + r * 128 + (((4 + q) ^ swz8(r)) << 4)));
     }
+    bf16x8 a0[8], a1[8];
+    int ix[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {  // 32 rows of 8 bytes per 256 B block, 4 bytes per lane
-      const int row = 32 * j + (lane >> 1);
-      moff[j] = (uint32_t)(row * (tk >> 3) + 4 * (lane & 1));
-    }
-    const uint8_t* xbase = reinterpret_cast<const uint8_t*>(x + m0 * ldx);
-    auto load_step = [&](int step) {
-      uint8_t* st = lds + (step % STAGES) * STAGE_BYTES;
-      const uint8_t* xb = xbase + (int64_t)step * BK * 2;
+    for (int h = 0; h < 2; ++h) {
+      const int dh = h ? d1 : d0;
+      const uint8_t* g = cur + X_BYTES + (2 * wn + h) * G_BYTES;
+      if (dh > 0) {
 #pragma unroll
-      for (int j = 0; j < BM / 8; ++j) g2l16(xb + xoff[j], st + 1024 * j);
-      const int kin = (step & ks) << 6;
-#pragma unroll 1
-      for (int grp = 0; grp < 4; ++grp) {
-        const int64_t gn0 = n0 + 64 * grp;
-        if (gn0 >= n) break;
-        const int32_t d = tile_desc[(gn0 >> ns) * tiles_k + (step >> ks)];
-        const int64_t slot = d >> 1;
-        const int64_t r0 = gn0 & (tn - 1);
-        uint8_t* g = st + X_BYTES + grp * G_BYTES;
-        if ((d & 1) == PATCH_TILE_DENSE) {
-          const uint8_t* src = reinterpret_cast<const uint8_t*>(dense_vals + slot * tn * tk + r0 * tk + kin);
+        for (int b4 = 0; b4 < 4; ++b4) {
+          a0[4 * h + b4] = lds8(g + 2048 * b4 + lane * 16);
+          a1[4 * h + b4] = lds8(g + 2048 * b4 + 1024 + lane * 16);
+          ix[4 * h + b4] = 0x4444;  // kept positions 0 and 1 of every group
+        }
+      } else if (dh == 0) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) g2l16(src + doff[j], g + 1024 * j);
-        } else {
-          const uint8_t* src =
-              reinterpret_cast<const uint8_t*>(sparse_vals + slot * tn * (tk >> 1) + r0 * (tk >> 1) + (kin >> 1));
-#pragma unroll
-          for (int j = 0; j < 4; ++j) g2l16(src + soff[j], g + 1024 * j);
-          const uint8_t* msrc = sparse_meta + slot * tn * (tk >> 3) + r0 * (tk >> 3) + (kin >> 3);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) g2l4(msrc + moff[j], g + 4096 + 256 * j);
+        for (int b4 = 0; b4 < 4; ++b4) {
+          a0[4 * h + b4] = lds8(g + 1024 * b4 + lane * 16);
+          ix[4 * h + b4] = *reinterpret_cast<const uint16_t*>(g + 4096 + 128 * b4 + 2 * lane);
         }
       }
-    };
-    if (p < nsteps) load_step(p);
-    for (int i = 0; i < nsteps; ++i) {
-      if ((i & 1) == p) wait_loads();  // step i is mine: it must have landed
-      wg_barrier();
-      if (i + 2 < nsteps && ((i + 2) & 1) == p) load_step(i + 2);  // into the stage step i - 1 used
     }
-    return;
-  }
-
-  // ------------------------------ consumer ------------------------------
-  const int q = lane >> 4, r16 = lane & 15;
-  const int64_t gn0 = n0 + 64 * wave;
-  const bool group_ok = gn0 < n;
-  const int64_t desc_row = (gn0 >> ns) * tiles_k;
-
-  f32x4 acc[4][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int h = 0; h < 2; ++h) {
+      const int dh = h ? d1 : d0;
+      if (dh < 0) continue;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const int bn = 4 * h + b4;
+          acc[bn][bm] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b[bm], acc[bn][bm], ix[bn], 0, 0);
+        }
+      if (dh > 0) {  // kept positions 2 and 3 of every group
+#pragma unroll
+        for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const int bn = 4 * h + b4;
+            acc[bn][bm] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a1[bn], b[bm], acc[bn][bm], 0xEEEE, 0, 0);
+          }
+      }
+    }
+  };
 
+  if (nsteps > 0) issue(0, 0);
   for (int i = 0; i < nsteps; ++i) {
-    wg_barrier();  // step i has landed; step i - 1's stage may now be refilled
-    if (!group_ok) continue;
-    const uint8_t* cur = lds + (i % STAGES) * STAGE_BYTES;
-    const uint8_t* g = cur + X_BYTES + wave * G_BYTES;
-    const bool dense = (tile_desc[desc_row + (i >> ks)] & 1) == PATCH_TILE_DENSE;
-    // W operands of the 4 row blocks: a lane covers dense k = 16q .. 16q + 15 of the step
-    bf16x8 a0[4], a1[4];
-    int i0[4];
-    if (dense) {
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn) {
-        const int r = 16 * bn + r16;
-        // 32 contiguous bytes: dword 2g = positions (0,1) of group g, dword 2g + 1 = (2,3)
-        const uint4 lo = *reinterpret_cast<const uint4*>(g + r * 128 + (((2 * q) ^ swz8(r)) << 4));
-        const uint4 hi = *reinterpret_cast<const uint4*>(g + r * 128 + (((2 * q + 1) ^ swz8(r)) << 4));
-        const uint4 e = make_uint4(lo.x, lo.z, hi.x, hi.z), o = make_uint4(lo.y, lo.w, hi.y, hi.w);
-        a0[bn] = *reinterpret_cast<const bf16x8*>(&e);
-        a1[bn] = *reinterpret_cast<const bf16x8*>(&o);
-        i0[bn] = 0x4444;  // kept positions 0 and 1 of every group
-      }
-    } else {
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn) {
-        const int r = 16 * bn + r16;
-        a0[bn] = lds8(g + r * 64 + ((q ^ swz4(r)) << 4));
-        i0[bn] = *reinterpret_cast<const uint16_t*>(g + 4096 + r * 8 + 2 * q);
-      }
-    }
-    // X operands streamed per 16-column block: k = 8q .. (regs 0-7) and 32 + 8q .. (regs 8-15)
-#pragma unroll
-    for (int bm = 0; bm < 8; ++bm) {
-      const int r = 16 * bm + r16;
-      const bf16x16 b = cat16(lds8(cur + r * 128 + ((q ^ swz8(r)) << 4)),
-                              lds8(cur + r * 128 + (((4 + q) ^ swz8(r)) << 4)));
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn)
-        acc[bn][bm] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b, acc[bn][bm], i0[bn], 0, 0);
-      if (dense) {
-#pragma unroll
-        for (int bn = 0; bn < 4; ++bn)  // kept positions 2 and 3 of every group
-          acc[bn][bm] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a1[bn], b, acc[bn][bm], 0xEEEE, 0, 0);
-      }
-    }
+    step_barrier();  // step i has landed in stage i & 1; stage (i + 1) & 1 is free
+    if (i + 1 < nsteps) issue(i + 1, (i + 1) & 1);
+    compute(i, i & 1);
   }
 
   // epilogue: per block, lane holds rows n = 4 q + (0..3) of column m = r16
-  if (!group_ok) return;
 #pragma unroll
-  for (int bm = 0; bm < 8; ++bm) {
-    const int64_t mm = m0 + 16 * bm + r16;
-    if (mm >= m) continue;
+  for (int h = 0; h < 2; ++h) {
+    if (h == 0 ? !hok0 : !hok1) continue;
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      const f32x4 v = acc[bn][bm];
-      store4<F32>(y, ldy, mm, gn0 + 16 * bn + 4 * q, v[0], v[1], v[2], v[3]);
+    for (int bm = 0; bm < 4; ++bm) {
+      const int64_t mm = m0 + 64 * wm + 16 * bm + r16;
+      if (mm >= m) continue;
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const int bn = 4 * h + b4;
+        const f32x4 v = acc[bn][bm];
+        store4<F32>(y, ldy, mm, wrow0 + 16 * bn + 4 * q, v[0], v[1], v[2], v[3]);
+      }
     }
   }
 }
@@ -473,7 +471,7 @@ hipError_t launch_gemm_stream(const patch_weight* pw, const uint16_t* x, int64_t
 
 hipError_t launch_gemm_tiled(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx, void* y,
                              int64_t ldy, int out_f32, hipStream_t s) {
-  constexpr int lds_bytes = tiled::STAGES * tiled::STAGE_BYTES;  // 144 KiB: opt in above 64 KiB, once
+  constexpr int lds_bytes = tiled::STAGES * tiled::STAGE_BYTES;  // 128 KiB: opt in above 64 KiB, once
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_tiled<true>),
@@ -484,13 +482,15 @@ hipError_t launch_gemm_tiled(const patch_weight* pw, const uint16_t* x, int64_t 
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid((unsigned)(((pw->n + tiled::BN - 1) / tiled::BN) * ((m + tiled::BM - 1) / tiled::BM)));
+  const int64_t blocks = ((pw->n + tiled::BN - 1) / tiled::BN) * ((m + tiled::BM - 1) / tiled::BM);
   if (out_f32)
-    hipLaunchKernelGGL(k_gemm_tiled<true>, grid, dim3(tiled::THREADS), lds_bytes, s, pw->tile_desc, pw->dense_vals,
-                       pw->sparse_vals, pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x, m, ldx, y, ldy);
+    hipLaunchKernelGGL(k_gemm_tiled<true>, dim3((unsigned)blocks), dim3(512), lds_bytes, s, pw->tile_desc,
+                       pw->dense_vals, pw->sparse_vals, pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x,
+                       m, ldx, y, ldy);
   else
-    hipLaunchKernelGGL(k_gemm_tiled<false>, grid, dim3(tiled::THREADS), lds_bytes, s, pw->tile_desc, pw->dense_vals,
-                       pw->sparse_vals, pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x, m, ldx, y, ldy);
+    hipLaunchKernelGGL(k_gemm_tiled<false>, dim3((unsigned)blocks), dim3(512), lds_bytes, s, pw->tile_desc,
+                       pw->dense_vals, pw->sparse_vals, pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x,
+                       m, ldx, y, ldy);
   return hipGetLastError();
 }
 

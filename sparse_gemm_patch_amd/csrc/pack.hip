@@ -132,9 +132,23 @@ __global__ __launch_bounds__(1024) void k_slot_scan(const uint8_t* __restrict__ 
   }
 }
 
-// One workgroup per tile.  Dense: copy the tile row-major.  2:4: each thread
-// takes 8 consecutive k of one row (two groups): two kept values per group in
-// ascending k, and one byte of codes (i0 | i1 << 2), even group low.
+// Device layout of the packed pools ("operand order").  The GEMM feeds W to
+// smfmac 16x16x64 as the A operand, one 16-row block and one 64-wide K step at
+// a time; lane l = 16 q + r of such an operand covers row r of the block and
+// dense k = 16 q .. 16 q + 15 of the step.  Each (step, block) unit of a tile
+// is stored as exactly those 64 lane values, in lane order, so one 16-byte load
+// per lane fetches a whole operand (1 KiB contiguous per wave):
+//   unit u = step * (TN / 16) + block, for step < TK / 64, block < TN / 16
+//   2:4 values  [slot] [u] [lane] 8 bf16: the 8 kept values of the lane's 16 k
+//                                         (two per group of four, ascending k)
+//   2:4 codes   [slot] [u] [lane] u16:    code of group g at bits 4 g .. 4 g + 3
+//   dense       [slot] [u] [0/1] [lane] 8 bf16: the lane's 16 k split into
+//                                         dwords 0, 2, 4, 6 (positions 0 and 1
+//                                         of each group) and dwords 1, 3, 5, 7
+//                                         (positions 2 and 3)
+// Pool sizes equal those of the row-major format; patch_export converts.
+
+// One workgroup per tile; one work item per (unit, lane).
 __global__ __launch_bounds__(kThreads) void k_compress(const uint16_t* __restrict__ w, int64_t ldw,
                                                        const uint8_t* __restrict__ bits, int64_t k, int order,
                                                        int tn, int tk, int64_t tiles_k,
@@ -146,35 +160,41 @@ __global__ __launch_bounds__(kThreads) void k_compress(const uint16_t* __restric
   const int64_t ti = t / tiles_k, tj = t % tiles_k;
   const int32_t d = tile_desc[t];
   const int64_t slot = d >> 1;
-  const uint16_t* wt = w + ti * tn * ldw + tj * tk;
-  const int units_per_row = tk >> 3;  // 8 bf16 = 16 bytes per unit
-  const int units = tn * units_per_row;
-  if ((d & 1) == PATCH_TILE_DENSE) {
-    uint16_t* dst = dense_vals + slot * tn * tk;
-    for (int u = threadIdx.x; u < units; u += kThreads) {
-      const int r = u / units_per_row, c = u % units_per_row;
-      *reinterpret_cast<uint4*>(dst + r * tk + c * 8) = *reinterpret_cast<const uint4*>(wt + r * ldw + c * 8);
-    }
-    return;
-  }
-  uint16_t* vdst = sparse_vals + slot * tn * (tk >> 1);
-  uint8_t* mdst = sparse_meta + slot * tn * (tk >> 3);
+  const int bt = tn >> 4;                   // 16-row blocks per tile
+  const int items = (tk >> 6) * bt * 64;
   const int64_t row_bytes = k >> 3;
-  const uint8_t* bt = bits + ti * tn * row_bytes + tj * (tk >> 3);
-  for (int u = threadIdx.x; u < units; u += kThreads) {
-    const int r = u / units_per_row, c = u % units_per_row;
-    const uint4 raw = *reinterpret_cast<const uint4*>(wt + r * ldw + c * 8);
-    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
-    uint32_t g0, g1;
-    byte_to_groups(bt[r * row_bytes + c], order, g0, g1);
-    const uint32_t a0 = __builtin_ctz(g0), b0 = 31 - __builtin_clz(g0);
-    const uint32_t a1 = __builtin_ctz(g1), b1 = 31 - __builtin_clz(g1);
+  for (int it = threadIdx.x; it < items; it += kThreads) {
+    const int u = it >> 6, l = it & 63;
+    const int step = u / bt, blk = u % bt, q = l >> 4, r = l & 15;
+    const int64_t row = ti * tn + blk * 16 + r;
+    const int64_t col = tj * tk + step * 64 + 16 * q;
+    const uint16_t* src = w + row * ldw + col;
+    const uint4 lo = *reinterpret_cast<const uint4*>(src);
+    const uint4 hi = *reinterpret_cast<const uint4*>(src + 8);
+    if ((d & 1) == PATCH_TILE_DENSE) {
+      uint8_t* dst = reinterpret_cast<uint8_t*>(dense_vals) + (slot * tn * tk + (int64_t)u * 1024) * 2 + l * 16;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.z, hi.x, hi.z);
+      *reinterpret_cast<uint4*>(dst + 1024) = make_uint4(lo.y, lo.w, hi.y, hi.w);
+      continue;
+    }
+    const uint32_t wv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     auto elem = [&](uint32_t e) -> uint32_t { return (wv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu; };
-    uint2 out;
-    out.x = elem(a0) | (elem(b0) << 16);
-    out.y = elem(4 + a1) | (elem(4 + b1) << 16);
-    *reinterpret_cast<uint2*>(vdst + r * (tk >> 1) + c * 4) = out;
-    mdst[r * (tk >> 3) + c] = (uint8_t)((a0 | (b0 << 2)) | ((a1 | (b1 << 2)) << 4));
+    const uint8_t* mb = bits + row * row_bytes + (col >> 3);  // 16 mask bits = 4 groups
+    uint32_t vals[4], meta = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t g0, g1;
+      byte_to_groups(mb[h], order, g0, g1);
+      const uint32_t a0 = __builtin_ctz(g0), b0 = 31 - __builtin_clz(g0);
+      const uint32_t a1 = __builtin_ctz(g1), b1 = 31 - __builtin_clz(g1);
+      const uint32_t base = 8 * h;
+      vals[2 * h] = elem(base + a0) | (elem(base + b0) << 16);
+      vals[2 * h + 1] = elem(base + 4 + a1) | (elem(base + 4 + b1) << 16);
+      meta |= ((a0 | (b0 << 2)) | ((a1 | (b1 << 2)) << 4)) << (8 * h);
+    }
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(sparse_vals) + slot * tn * tk + (int64_t)u * 1024 + l * 16) =
+        make_uint4(vals[0], vals[1], vals[2], vals[3]);
+    *reinterpret_cast<uint16_t*>(sparse_meta + slot * tn * (tk >> 3) + (int64_t)u * 128 + l * 2) = (uint16_t)meta;
   }
 }
 
@@ -189,34 +209,37 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const int32_t* __restri
   const int64_t ti = t / tiles_k, tj = t % tiles_k;
   const int32_t d = tile_desc[t];
   const int64_t slot = d >> 1;
-  uint16_t* ot = out + ti * tn * ldw + tj * tk;
-  const int units_per_row = tk >> 3;
-  const int units = tn * units_per_row;
-  if ((d & 1) == PATCH_TILE_DENSE) {
-    const uint16_t* src = dense_vals + slot * tn * tk;
-    for (int u = threadIdx.x; u < units; u += kThreads) {
-      const int r = u / units_per_row, c = u % units_per_row;
-      *reinterpret_cast<uint4*>(ot + r * ldw + c * 8) = *reinterpret_cast<const uint4*>(src + r * tk + c * 8);
+  const int bt = tn >> 4;
+  const int items = (tk >> 6) * bt * 64;
+  for (int it = threadIdx.x; it < items; it += kThreads) {
+    const int u = it >> 6, l = it & 63;
+    const int step = u / bt, blk = u % bt, q = l >> 4, r = l & 15;
+    uint16_t* dst = out + (ti * tn + blk * 16 + r) * ldw + tj * tk + step * 64 + 16 * q;
+    if ((d & 1) == PATCH_TILE_DENSE) {
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(dense_vals) + (slot * tn * tk + (int64_t)u * 1024) * 2 + l * 16;
+      const uint4 e = *reinterpret_cast<const uint4*>(src);
+      const uint4 o = *reinterpret_cast<const uint4*>(src + 1024);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(e.x, o.x, e.y, o.y);
+      *reinterpret_cast<uint4*>(dst + 8) = make_uint4(e.z, o.z, e.w, o.w);
+      continue;
     }
-    return;
-  }
-  const uint16_t* vsrc = sparse_vals + slot * tn * (tk >> 1);
-  const uint8_t* msrc = sparse_meta + slot * tn * (tk >> 3);
-  for (int u = threadIdx.x; u < units; u += kThreads) {
-    const int r = u / units_per_row, c = u % units_per_row;
-    const uint2 v = *reinterpret_cast<const uint2*>(vsrc + r * (tk >> 1) + c * 4);
-    const uint32_t code = msrc[r * (tk >> 3) + c];
-    uint32_t e[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    e[code & 3u] = v.x & 0xFFFFu;
-    e[(code >> 2) & 3u] = v.x >> 16;
-    e[4 + ((code >> 4) & 3u)] = v.y & 0xFFFFu;
-    e[4 + ((code >> 6) & 3u)] = v.y >> 16;
-    uint4 o;
-    o.x = e[0] | (e[1] << 16);
-    o.y = e[2] | (e[3] << 16);
-    o.z = e[4] | (e[5] << 16);
-    o.w = e[6] | (e[7] << 16);
-    *reinterpret_cast<uint4*>(ot + r * ldw + c * 8) = o;
+    const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(sparse_vals) + slot * tn * tk +
+                                                     (int64_t)u * 1024 + l * 16);
+    const uint32_t meta = *reinterpret_cast<const uint16_t*>(sparse_meta + slot * tn * (tk >> 3) + (int64_t)u * 128 + l * 2);
+    const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+    uint32_t e[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[i] = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t code = (meta >> (4 * g)) & 0xFu;
+      e[4 * g + (code & 3u)] = vv[g] & 0xFFFFu;
+      e[4 * g + (code >> 2)] = vv[g] >> 16;
+    }
+    *reinterpret_cast<uint4*>(dst) = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                                                e[6] | (e[7] << 16));
+    *reinterpret_cast<uint4*>(dst + 8) = make_uint4(e[8] | (e[9] << 16), e[10] | (e[11] << 16),
+                                                    e[12] | (e[13] << 16), e[14] | (e[15] << 16));
   }
 }
 
