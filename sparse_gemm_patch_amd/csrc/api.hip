@@ -385,7 +385,8 @@ patch_status patch_export(const patch_weight* w, uint8_t* tile_map, int32_t* til
         for (int64_t b = 0; b < tk / 8; ++b) {
           const int64_t step = b / 8, bb = b % 8, q = bb / 2;
           const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16;
-          sparse_meta[(s * tn + row) * (tk / 8) + b] = tmp[s * tn * tk / 8 + u * 128 + lane * 2 + (bb & 1)];
+          sparse_meta[(s * tn + row) * (tk / 8) + b] =
+              tmp[s * tn * tk / 8 + (u >> 2) * 512 + lane * 8 + (u & 3) * 2 + (bb & 1)];
         }
   }
   return ok();

@@ -119,16 +119,15 @@ __global__ __launch_bounds__(256) void k_gemm_stream(
       }
     } else {
       const uint8_t* vt = reinterpret_cast<const uint8_t*>(sparse_vals) + slot * tn * tk + (int64_t)u0 * 1024 + lane * 16;
-      const uint8_t* mt = sparse_meta + slot * tn * (tk >> 3) + (int64_t)u0 * 128 + lane * 2;
+      // codes of the four blocks: 8 bytes per lane; abid picks the 16-bit half
+      const uint2 codes = *reinterpret_cast<const uint2*>(sparse_meta + slot * tn * (tk >> 3) + (int64_t)(u0 >> 2) * 512 + lane * 8);
       bf16x8 a[4];
-      int idx[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        a[b] = *reinterpret_cast<const bf16x8*>(vt + b * 1024);
-        idx[b] = *reinterpret_cast<const uint16_t*>(mt + b * 128);
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[b] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[b], xb, acc[b], idx[b], 0, 0);
+      for (int b = 0; b < 4; ++b) a[b] = *reinterpret_cast<const bf16x8*>(vt + b * 1024);
+      acc[0] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[0], xb, acc[0], (int)codes.x, 0, 0);
+      acc[1] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[1], xb, acc[1], (int)codes.x, 0, 1);
+      acc[2] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[2], xb, acc[2], (int)codes.y, 0, 0);
+      acc[3] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[3], xb, acc[3], (int)codes.y, 0, 1);
     }
   }
 
@@ -193,20 +192,22 @@ __global__ __launch_bounds__(256) void k_gemm_stream(
 // fp32 accumulators per lane, two waves per SIMD.  K advances 64 at a time; a
 // step never crosses a tile.
 //
-// What bounds this kernel on MI355X is how fast a CU can pull operands out of
-// L2 (about 130 GB/s per CU, reached only when several waves issue loads).  A
-// 256 x 256 block needs 50 KiB (2:4) to 64 KiB (dense) per step for 8.4
-// dense-equivalent MFLOP, which keeps the sparse MFMA rate within reach.
+// What bounds this kernel on MI355X is LDS traffic: per step a CU writes
+// 50 KiB (2:4) to 64 KiB (dense) into LDS and its waves read 136 to 192 KiB
+// back, at 256 bytes per clock for conflict-free 16-byte reads, next to 64
+// (2:4) to 128 (dense) MFMAs of 16 x 16 x 64 per SIMD at 16 clocks each.
+// Every LDS access pattern below runs at the full rate.
 //
 // LDS holds two stages of 64 KiB:
-//   X  256 rows x 128 B; 16-byte chunk c of row r at position c ^ h(r),
-//      h(r) = (r & 7) ^ ((r >> 3) & 1), so the 16-byte reads of 16 consecutive
-//      lanes (16 rows, one chunk) fall on distinct banks.
+//   X  256 rows x 128 B; 16-byte chunk c of row r at position c ^ (r & 7).
+//      The B-operand reads (16 rows, one chunk per 16 lanes) then run at the
+//      full 256 B per clock; without the swizzle they run at a quarter of it.
 //   W  four 64-row groups of 8 KiB.  A group's operands for one step are
 //      contiguous in the operand-order pools and are copied verbatim: dense 4
-//      blocks x [a0 | a1] x 1 KiB; 2:4 4 blocks x 1 KiB of values, then 4 x
-//      128 B of codes at +4 KiB.  Lane l reads bytes 16 l .. 16 l + 15 of a
-//      block, which no bank conflict can touch.
+//      blocks x [a0 | a1] x 1 KiB; 2:4 4 blocks x 1 KiB of values, then 512 B
+//      of codes at +4 KiB, 8 bytes per lane (one code word per block).  Lane l
+//      reads bytes 16 l .. 16 l + 15 of a block (or 8 l .. 8 l + 7 of the
+//      codes): consecutive lanes, consecutive addresses.
 // Every wave copies its share of each step (32 X rows and a quarter of the W
 // data, always 8 copy instructions) straight from global memory into LDS with
 // global_load_lds, one step ahead, then waits for its own copies before the
@@ -242,7 +243,7 @@ __device__ __forceinline__ void step_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 __device__ __forceinline__ bf16x8 lds8(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int xswz(int r) { return r & 7; }
 
 // Output block of this workgroup.  The dispatcher deals workgroup i to XCD
 // i % 8; renumbering so that each XCD owns a contiguous range of blocks, walked
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
     const int row = 32 * wave + 8 * j + (lane >> 3);
     int64_t gm = m0 + row;
     if (gm > m - 1) gm = m - 1;
-    xp[j] = x + gm * ldx + 8 * ((lane & 7) ^ swz8(row));
+    xp[j] = x + gm * ldx + 8 * ((lane & 7) ^ xswz(row));
   }
   const int cg = wave >> 1, chalf = wave & 1;  // copied group and half of its copies
   const int64_t gn0 = n0 + 64 * cg;
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
 #pragma unroll
       for (int j = 0; j < 4; ++j) dma16(src + 1024 * j, g + 1024 * j);
     } else {
-      const uint8_t* mp = msrc + slot * tn * (tk >> 3) + u0 * 128;
+      const uint8_t* mp = msrc + slot * tn * (tk >> 3) + (u0 >> 2) * 512;
 #pragma unroll
       for (int j = 0; j < 4; ++j) dma4(mp + 256 * (j & 1), g + 4096 + 256 * (j & 1));
     }
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm) {
       const int r = 64 * wm + 16 * bm + r16;
-      b[bm] = cat16(lds8(cur + r * 128 + ((q ^ swz8(r)) << 4)), lds8(cur + r * 128 + (((4 + q) ^ swz8(r)) << 4)));
+      b[bm] = cat16(lds8(cur + r * 128 + ((q ^ xswz(r)) << 4)), lds8(cur + r * 128 + (((4 + q) ^ xswz(r)) << 4)));
     }
     bf16x8 a0[8], a1[8];
     int ix[8];
@@ -369,14 +370,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
         for (int b4 = 0; b4 < 4; ++b4) {
           a0[4 * h + b4] = lds8(g + 2048 * b4 + lane * 16);
           a1[4 * h + b4] = lds8(g + 2048 * b4 + 1024 + lane * 16);
-          ix[4 * h + b4] = 0x4444;  // kept positions 0 and 1 of every group
+          ix[4 * h + b4] = 0x44444444;  // kept positions 0 and 1 of every group, in both halves
         }
       } else if (dh == 0) {
 #pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4) {
-          a0[4 * h + b4] = lds8(g + 1024 * b4 + lane * 16);
-          ix[4 * h + b4] = *reinterpret_cast<const uint16_t*>(g + 4096 + 128 * b4 + 2 * lane);
-        }
+        for (int b4 = 0; b4 < 4; ++b4) a0[4 * h + b4] = lds8(g + 1024 * b4 + lane * 16);
+        const uint2 c = *reinterpret_cast<const uint2*>(g + 4096 + 8 * lane);
+        ix[4 * h + 0] = (int)c.x;
+        ix[4 * h + 1] = (int)c.x;
+        ix[4 * h + 2] = (int)c.y;
+        ix[4 * h + 3] = (int)c.y;
       }
     }
 #pragma unroll
@@ -388,7 +391,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) {
           const int bn = 4 * h + b4;
-          acc[bn][bm] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b[bm], acc[bn][bm], ix[bn], 0, 0);
+          // odd blocks of a 2:4 group take the upper 16 bits of their code word
+          acc[bn][bm] = b4 & 1 ? __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b[bm], acc[bn][bm], ix[bn], 0, 1)
+                               : __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b[bm], acc[bn][bm], ix[bn], 0, 0);
         }
       if (dh > 0) {  // kept positions 2 and 3 of every group
 #pragma unroll

@@ -141,7 +141,10 @@ __global__ __launch_bounds__(1024) void k_slot_scan(const uint8_t* __restrict__ 
 //   unit u = step * (TN / 16) + block, for step < TK / 64, block < TN / 16
 //   2:4 values  [slot] [u] [lane] 8 bf16: the 8 kept values of the lane's 16 k
 //                                         (two per group of four, ascending k)
-//   2:4 codes   [slot] [u] [lane] u16:    code of group g at bits 4 g .. 4 g + 3
+//   2:4 codes   [slot] [u / 4] [lane] [u % 4] u16: code of group g at bits
+//                                         4 g .. 4 g + 3; the codes of the four
+//                                         blocks of a 64-row group sit together,
+//                                         8 bytes per lane
 //   dense       [slot] [u] [0/1] [lane] 8 bf16: the lane's 16 k split into
 //                                         dwords 0, 2, 4, 6 (positions 0 and 1
 //                                         of each group) and dwords 1, 3, 5, 7
@@ -194,7 +197,8 @@ __global__ __launch_bounds__(kThreads) void k_compress(const uint16_t* __restric
     }
     *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(sparse_vals) + slot * tn * tk + (int64_t)u * 1024 + l * 16) =
         make_uint4(vals[0], vals[1], vals[2], vals[3]);
-    *reinterpret_cast<uint16_t*>(sparse_meta + slot * tn * (tk >> 3) + (int64_t)u * 128 + l * 2) = (uint16_t)meta;
+    *reinterpret_cast<uint16_t*>(sparse_meta + slot * tn * (tk >> 3) + (int64_t)(u >> 2) * 512 + l * 8 + (u & 3) * 2) =
+        (uint16_t)meta;
   }
 }
 
@@ -225,7 +229,8 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const int32_t* __restri
     }
     const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(sparse_vals) + slot * tn * tk +
                                                      (int64_t)u * 1024 + l * 16);
-    const uint32_t meta = *reinterpret_cast<const uint16_t*>(sparse_meta + slot * tn * (tk >> 3) + (int64_t)u * 128 + l * 2);
+    const uint32_t meta = *reinterpret_cast<const uint16_t*>(sparse_meta + slot * tn * (tk >> 3) +
+                                                            (int64_t)(u >> 2) * 512 + l * 8 + (u & 3) * 2);
     const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
     uint32_t e[16];
 #pragma unroll
