@@ -135,13 +135,15 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
 patch_status patch_gemm(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx,
                         void* y, int64_t ldy, patch_out_dtype y_dtype, void* stream);
 
-/* patch_gemm with the kernel chosen by the caller.  split_k <= 0 lets the
- * library choose; for PATCH_KERNEL_STREAM a positive value forces the number
- * of K slices (clamped to [1, tiles along K * TK/64]).  PATCH_KERNEL_STREAM
- * needs m <= 16. */
+/* patch_gemm with the kernel chosen by the caller, for tests and measurements.
+ * `variant` <= 0 lets the library choose; a positive value forces
+ *   PATCH_KERNEL_STREAM: the number of K slices (clamped to [1, K / 64]);
+ *   PATCH_KERNEL_TILED:  the X rows per workgroup, 256, 128 or 64 (other
+ *                        values: PATCH_E_INVALID_ARG);
+ * and is ignored under PATCH_KERNEL_AUTO.  PATCH_KERNEL_STREAM needs m <= 16. */
 patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx,
                                void* y, int64_t ldy, patch_out_dtype y_dtype,
-                               patch_kernel kernel, int32_t split_k, void* stream);
+                               patch_kernel kernel, int32_t variant, void* stream);
 
 /*
  * patch_unpack -- rebuild the masked dense weight: the card's "apply the mask"

@@ -245,7 +245,7 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
 }
 
 static patch_status gemm_common(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y,
-                                int64_t ldy, patch_out_dtype y_dtype, patch_kernel kernel, int32_t split_k,
+                                int64_t ldy, patch_out_dtype y_dtype, patch_kernel kernel, int32_t variant,
                                 void* stream) {
   if (!w) return fail(PATCH_E_INVALID_ARG, "weight handle is NULL");
   if (y_dtype != PATCH_OUT_BF16 && y_dtype != PATCH_OUT_F32)
@@ -255,6 +255,8 @@ static patch_status gemm_common(const patch_weight* w, const uint16_t* x, int64_
   if (m < 0) return fail(PATCH_E_INVALID_ARG, "m = %lld < 0", (long long)m);
   if (kernel == PATCH_KERNEL_STREAM && m > 16)
     return fail(PATCH_E_INVALID_ARG, "the streaming kernel takes m <= 16, got %lld", (long long)m);
+  if (kernel == PATCH_KERNEL_TILED && variant > 0 && variant != 256 && variant != 128 && variant != 64)
+    return fail(PATCH_E_INVALID_ARG, "tiled block rows must be 256, 128 or 64, got %d", (int)variant);
   if (m == 0 || w->n == 0) return ok();
   if (!y) return fail(PATCH_E_INVALID_ARG, "y is NULL");
   if (!aligned16(y)) return fail(PATCH_E_INVALID_ARG, "y must be 16-byte aligned");
@@ -275,8 +277,9 @@ static patch_status gemm_common(const patch_weight* w, const uint16_t* x, int64_
     e = launch_fill_zero_y(y, m, w->n, ldy, f32, s);
   } else {
     const bool stream_kernel = kernel == PATCH_KERNEL_STREAM || (kernel == PATCH_KERNEL_AUTO && m <= 16);
-    e = stream_kernel ? launch_gemm_stream(w, x, m, ldx, y, ldy, f32, split_k, s)
-                      : launch_gemm_tiled(w, x, m, ldx, y, ldy, f32, s);
+    const int32_t v = kernel == PATCH_KERNEL_AUTO ? 0 : variant;
+    e = stream_kernel ? launch_gemm_stream(w, x, m, ldx, y, ldy, f32, v, s)
+                      : launch_gemm_tiled(w, x, m, ldx, y, ldy, f32, v, s);
   }
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return ok();
@@ -288,9 +291,9 @@ patch_status patch_gemm(const patch_weight* w, const uint16_t* x, int64_t m, int
 }
 
 patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y,
-                               int64_t ldy, patch_out_dtype y_dtype, patch_kernel kernel, int32_t split_k,
+                               int64_t ldy, patch_out_dtype y_dtype, patch_kernel kernel, int32_t variant,
                                void* stream) {
-  return gemm_common(w, x, m, ldx, y, ldy, y_dtype, kernel, split_k, stream);
+  return gemm_common(w, x, m, ldx, y, ldy, y_dtype, kernel, variant, stream);
 }
 
 patch_status patch_unpack(const patch_weight* w, uint16_t* w_out, int64_t ldw, void* stream) {

@@ -186,11 +186,15 @@ __global__ __launch_bounds__(256) void k_gemm_stream(
 // Tiled kernel for prefill-sized M.
 //
 // Workgroup = 8 waves in a 2 x 4 grid; the block of Y^T is 256 W rows (n) x
-// 256 X rows (m).  Wave (wn, wm) owns W rows 128 wn .. +127 (8 row blocks of
-// 16, in two 64-row groups that each lie in one tile row) and X rows
-// 64 wm .. +63 (4 column blocks): 8 x 4 accumulator blocks of 16 x 16, 128
-// fp32 accumulators per lane, two waves per SIMD.  K advances 64 at a time; a
-// step never crosses a tile.
+// BM X rows (m), BM = 256, 128 or 64.  Wave (wn, wm) owns W rows 128 wn .. +127
+// (8 row blocks of 16, in two 64-row groups that each lie in one tile row) and
+// X rows BM/4 wm .. +BM/4-1 (BM/64 column blocks): up to 8 x 4 accumulator
+// blocks of 16 x 16, 128 fp32 accumulators per lane, two waves per SIMD.  K
+// advances 64 at a time; a step never crosses a tile.  The smaller BM exist
+// for shapes whose 256 x 256 blocks would leave CUs idle: they cost more LDS
+// traffic per flop, but no block has to be split along K (a cross-workgroup
+// reduction needs device-scope fences, which on this chip write back the
+// whole L2 of an XCD).
 //
 // What bounds this kernel on MI355X is LDS traffic: per step a CU writes
 // 50 KiB (2:4) to 64 KiB (dense) into LDS and its waves read 136 to 192 KiB
@@ -198,8 +202,8 @@ __global__ __launch_bounds__(256) void k_gemm_stream(
 // (2:4) to 128 (dense) MFMAs of 16 x 16 x 64 per SIMD at 16 clocks each.
 // Every LDS access pattern below runs at the full rate.
 //
-// LDS holds two stages of 64 KiB:
-//   X  256 rows x 128 B; 16-byte chunk c of row r at position c ^ (r & 7).
+// LDS holds two stages of BM * 128 + 32 KiB:
+//   X  BM rows x 128 B; 16-byte chunk c of row r at position c ^ (r & 7).
 //      The B-operand reads (16 rows, one chunk per 16 lanes) then run at the
 //      full 256 B per clock; without the swizzle they run at a quarter of it.
 //   W  four 64-row groups of 8 KiB.  A group's operands for one step are
@@ -208,8 +212,8 @@ __global__ __launch_bounds__(256) void k_gemm_stream(
 //      of codes at +4 KiB, 8 bytes per lane (one code word per block).  Lane l
 //      reads bytes 16 l .. 16 l + 15 of a block (or 8 l .. 8 l + 7 of the
 //      codes): consecutive lanes, consecutive addresses.
-// Every wave copies its share of each step (32 X rows and a quarter of the W
-// data, always 8 copy instructions) straight from global memory into LDS with
+// Every wave copies its share of each step (BM/8 X rows and a quarter of the
+// W data) straight from global memory into LDS with
 // global_load_lds, one step ahead, then waits for its own copies before the
 // step's barrier.  The copies are issued from inline assembly (which saves and
 // restores M0, the LDS address register): the compiler cannot tell that they
@@ -218,12 +222,12 @@ __global__ __launch_bounds__(256) void k_gemm_stream(
 // explicit waits are the only ones these copies need.
 // ------------------------------------------------------------------------
 namespace tiled {
-constexpr int BN = 256, BM = 256, BK = 64;
-constexpr int X_BYTES = BM * 128;          // 32 KiB
+constexpr int BN = 256, BK = 64;
 constexpr int G_BYTES = 64 * 128;          // 8 KiB per 64-row W group
-constexpr int STAGE_BYTES = X_BYTES + 4 * G_BYTES;
 constexpr int STAGES = 2;
 constexpr int GROUP_N = 4;                 // block columns per group of the block order
+template <int BM> constexpr int x_bytes() { return BM * 128; }
+template <int BM> constexpr int stage_bytes() { return x_bytes<BM>() + 4 * G_BYTES; }
 }  // namespace tiled
 
 // global -> LDS copy of 16 (or 4) bytes per lane; lane i writes LDS bytes
@@ -250,6 +254,7 @@ __device__ __forceinline__ int xswz(int r) { return r & 7; }
 // in groups of GROUP_N block columns (m fastest inside a group), makes the
 // workgroups resident on one XCD cover a compact region and share their W and
 // X in that XCD's L2.
+template <int BM>
 __device__ __forceinline__ void block_origin(int64_t n, int64_t m, int64_t& n0, int64_t& m0) {
   using namespace tiled;
   const int nbn = (int)((n + BN - 1) / BN), nbm = (int)((m + BM - 1) / BM);
@@ -265,13 +270,15 @@ __device__ __forceinline__ void block_origin(int64_t n, int64_t m, int64_t& n0, 
   m0 = (int64_t)(in_group / width) * BM;
 }
 
-template <bool F32>
+template <bool F32, int BM>
 __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
     const int32_t* __restrict__ tile_desc, const uint16_t* __restrict__ dense_vals,
     const uint16_t* __restrict__ sparse_vals, const uint8_t* __restrict__ sparse_meta, int tn, int tk,
     int64_t tiles_k, int64_t n, int64_t k, const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
     void* __restrict__ y, int64_t ldy) {
   using namespace tiled;
+  constexpr int XB = BM / 64;                        // X blocks of 16 rows per wave
+  constexpr int X_BYTES = x_bytes<BM>(), STAGE_BYTES = stage_bytes<BM>();
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
@@ -280,19 +287,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
   const int wn = wave >> 2, wm = wave & 3;
   const int q = lane >> 4, r16 = lane & 15;
   int64_t n0, m0;
-  block_origin(n, m, n0, m0);
+  block_origin<BM>(n, m, n0, m0);
   const int nsteps = (int)(k / BK);
   const int ks = tk == 128;           // 64-wide K steps per tile column: 1 << ks
   const int ns = tn == 128 ? 7 : 6;   // log2(TN)
   const int bt = tn >> 4;             // 16-row blocks per tile
 
-  // ---- copy roles: X rows 32 wave + 8 j + (lane >> 3), logical chunk (lane & 7) ^ h(row)
+  // ---- copy roles: X rows BM/8 wave + 8 j + (lane >> 3), logical chunk (lane & 7) ^ (row & 7)
   // (rows past M clamp to M - 1: they only feed Y rows that are never stored),
   // and half (wave & 1) of W group wave >> 1 (rows n0 + 64 (wave >> 1) .. +63).
-  const uint16_t* xp[4];
+  const uint16_t* xp[XB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 32 * wave + 8 * j + (lane >> 3);
+  for (int j = 0; j < XB; ++j) {
+    const int row = BM / 8 * wave + 8 * j + (lane >> 3);
     int64_t gm = m0 + row;
     if (gm > m - 1) gm = m - 1;
     xp[j] = x + gm * ldx + 8 * ((lane & 7) ^ xswz(row));
@@ -306,20 +313,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
   const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(sparse_vals) + lane * 16;
   const uint8_t* msrc = sparse_meta + lane * 4;
 
-  // 8 copies per wave and step, whatever the tile types, so that the waits
-  // before each barrier are the same.  A group's 8 KiB: dense = 8 blocks of
-  // 1 KiB (half h copies blocks 4 h .. 4 h + 3); 2:4 = 4 value blocks (half 0)
-  // and 512 B of codes (half 1: two 256 B copies, each issued twice).
+  // A group's 8 KiB: dense = 8 blocks of 1 KiB (half h copies blocks
+  // 4 h .. 4 h + 3); 2:4 = 4 value blocks (half 0) and 512 B of codes (half 1,
+  // two 256 B copies).  The barrier waits for all of a wave's copies, so their
+  // number may differ between waves.
   auto issue = [&](int step, int stage) {
     const uint32_t st = lds_base + stage * STAGE_BYTES;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(xp[j] + step * 64, st + (32 * wave + 8 * j) * 128);
+    for (int j = 0; j < XB; ++j) dma16(xp[j] + step * 64, st + (BM / 8 * wave + 8 * j) * 128);
     const uint32_t g = st + X_BYTES + cg * G_BYTES;
-    if (!g_ok) {  // group past N: keep the count with harmless copies into its unused slot
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(xp[j] + step * 64, g + 1024 * (4 * chalf + j));
-      return;
-    }
+    if (!g_ok) return;  // group past N
     const int32_t d = tile_desc[g_desc + (step >> ks)];
     const int64_t slot = d >> 1;
     const int64_t u0 = (step & ks) * bt + g_blk;  // first operand unit of the group
@@ -333,30 +336,30 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
       for (int j = 0; j < 4; ++j) dma16(src + 1024 * j, g + 1024 * j);
     } else {
       const uint8_t* mp = msrc + slot * tn * (tk >> 3) + (u0 >> 2) * 512;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dma4(mp + 256 * (j & 1), g + 4096 + 256 * (j & 1));
+      dma4(mp, g + 4096);
+      dma4(mp + 256, g + 4096 + 256);
     }
   };
 
-  // ---- compute role: W rows 128 wn .. +127 (groups 2 wn, 2 wn + 1), X rows 64 wm .. +63
+  // ---- compute role: W rows 128 wn .. +127 (groups 2 wn, 2 wn + 1), X rows BM/4 wm .. +BM/4-1
   const int64_t wrow0 = n0 + 128 * wn;
   const bool hok0 = wrow0 < n, hok1 = wrow0 + 64 < n;
   const int64_t hdesc0 = (wrow0 >> ns) * tiles_k, hdesc1 = ((wrow0 + 64) >> ns) * tiles_k;
 
-  f32x4 acc[8][4];
+  f32x4 acc[8][XB];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < XB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int step, int stage) {
     const uint8_t* cur = lds + stage * STAGE_BYTES;
     const int d0 = hok0 ? ((tile_desc[hdesc0 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
     const int d1 = hok1 ? ((tile_desc[hdesc1 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
-    bf16x16 b[4];
+    bf16x16 b[XB];
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm) {
-      const int r = 64 * wm + 16 * bm + r16;
+    for (int bm = 0; bm < XB; ++bm) {
+      const int r = BM / 4 * wm + 16 * bm + r16;
       b[bm] = cat16(lds8(cur + r * 128 + ((q ^ xswz(r)) << 4)), lds8(cur + r * 128 + (((4 + q) ^ xswz(r)) << 4)));
     }
     bf16x8 a0[8], a1[8];
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
       const int dh = h ? d1 : d0;
       if (dh < 0) continue;
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
+      for (int bm = 0; bm < XB; ++bm)
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) {
           const int bn = 4 * h + b4;
@@ -397,7 +400,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
         }
       if (dh > 0) {  // kept positions 2 and 3 of every group
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm)
+        for (int bm = 0; bm < XB; ++bm)
 #pragma unroll
           for (int b4 = 0; b4 < 4; ++b4) {
             const int bn = 4 * h + b4;
@@ -419,8 +422,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
   for (int h = 0; h < 2; ++h) {
     if (h == 0 ? !hok0 : !hok1) continue;
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm) {
-      const int64_t mm = m0 + 64 * wm + 16 * bm + r16;
+    for (int bm = 0; bm < XB; ++bm) {
+      const int64_t mm = m0 + BM / 4 * wm + 16 * bm + r16;
       if (mm >= m) continue;
 #pragma unroll
       for (int b4 = 0; b4 < 4; ++b4) {
@@ -474,29 +477,57 @@ hipError_t launch_gemm_stream(const patch_weight* pw, const uint16_t* x, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_tiled(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx, void* y,
-                             int64_t ldy, int out_f32, hipStream_t s) {
-  constexpr int lds_bytes = tiled::STAGES * tiled::STAGE_BYTES;  // 128 KiB: opt in above 64 KiB, once
+namespace {
+template <bool F32, int BM>
+hipError_t launch_tiled_bm(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx, void* y, int64_t ldy,
+                           hipStream_t s) {
+  constexpr int lds_bytes = tiled::STAGES * tiled::stage_bytes<BM>();  // above 64 KiB: opt in, once
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_tiled<true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_tiled<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_tiled<F32, BM>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t blocks = ((pw->n + tiled::BN - 1) / tiled::BN) * ((m + tiled::BM - 1) / tiled::BM);
-  if (out_f32)
-    hipLaunchKernelGGL(k_gemm_tiled<true>, dim3((unsigned)blocks), dim3(512), lds_bytes, s, pw->tile_desc,
-                       pw->dense_vals, pw->sparse_vals, pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x,
-                       m, ldx, y, ldy);
-  else
-    hipLaunchKernelGGL(k_gemm_tiled<false>, dim3((unsigned)blocks), dim3(512), lds_bytes, s, pw->tile_desc,
-                       pw->dense_vals, pw->sparse_vals, pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x,
-                       m, ldx, y, ldy);
+  const int64_t blocks = ((pw->n + tiled::BN - 1) / tiled::BN) * ((m + BM - 1) / BM);
+  hipLaunchKernelGGL((k_gemm_tiled<F32, BM>), dim3((unsigned)blocks), dim3(512), lds_bytes, s, pw->tile_desc,
+                     pw->dense_vals, pw->sparse_vals, pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x,
+                     m, ldx, y, ldy);
   return hipGetLastError();
+}
+}  // namespace
+
+int tiled_block_m(int64_t n, int64_t m) {
+  // Estimated time ~ rounds of 256 workgroups x the block's cost, where a
+  // block of BM rows costs BM / 256 of a full one divided by its relative
+  // efficiency (smaller blocks move more LDS bytes per flop).
+  const int bms[3] = {256, 128, 64};
+  const double eff[3] = {1.0, 0.69, 0.42};  // measured on the LLaMA-3.2-1B projections
+  const int64_t nbn = (n + tiled::BN - 1) / tiled::BN;
+  int best = 256;
+  double best_t = 0;
+  for (int i = 0; i < 3; ++i) {
+    const int64_t blocks = nbn * ((m + bms[i] - 1) / bms[i]);
+    const double t = (double)((blocks + 255) / 256) * bms[i] / 256.0 / eff[i];
+    if (i == 0 || t < best_t - 1e-9) {
+      best = bms[i];
+      best_t = t;
+    }
+  }
+  return best;
+}
+
+hipError_t launch_gemm_tiled(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx, void* y,
+                             int64_t ldy, int out_f32, int block_m, hipStream_t s) {
+  const int bm = block_m > 0 ? block_m : tiled_block_m(pw->n, m);
+  switch (bm) {
+    case 64:
+      return out_f32 ? launch_tiled_bm<true, 64>(pw, x, m, ldx, y, ldy, s) : launch_tiled_bm<false, 64>(pw, x, m, ldx, y, ldy, s);
+    case 128:
+      return out_f32 ? launch_tiled_bm<true, 128>(pw, x, m, ldx, y, ldy, s) : launch_tiled_bm<false, 128>(pw, x, m, ldx, y, ldy, s);
+    default:
+      return out_f32 ? launch_tiled_bm<true, 256>(pw, x, m, ldx, y, ldy, s) : launch_tiled_bm<false, 256>(pw, x, m, ldx, y, ldy, s);
+  }
 }
 
 hipError_t launch_fill_zero_y(void* y, int64_t m, int64_t n, int64_t ldy, int out_f32, hipStream_t s) {

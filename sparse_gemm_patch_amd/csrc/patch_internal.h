@@ -54,8 +54,10 @@ hipError_t launch_mask_unpack(const uint8_t* bits, int64_t count, int order, uin
 // ---- GEMM kernels ----
 hipError_t launch_gemm_stream(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx,
                               void* y, int64_t ldy, int out_f32, int split_k, hipStream_t s);
+// block_m: X rows per workgroup (256, 128 or 64); 0 lets tiled_block_m choose.
 hipError_t launch_gemm_tiled(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx,
-                             void* y, int64_t ldy, int out_f32, hipStream_t s);
+                             void* y, int64_t ldy, int out_f32, int block_m, hipStream_t s);
+int tiled_block_m(int64_t n, int64_t m);
 hipError_t launch_fill_zero_y(void* y, int64_t m, int64_t n, int64_t ldy, int out_f32, hipStream_t s);
 // Split count the streaming kernel uses when the caller does not force one.
 int stream_default_splits(const patch_weight* pw, int64_t m);

@@ -234,6 +234,39 @@ def test_stream_split_k_and_determinism(P, split_k):
     assert O.rel_error(y_host(y1), ref) <= TOL
 
 
+@pytest.mark.parametrize("block_m", [256, 128, 64])
+@pytest.mark.parametrize("tn,tk,frac", [(128, 128, 0.5), (64, 64, 0.9), (128, 64, 0.0), (64, 128, 1.0)])
+def test_tiled_block_rows(P, block_m, tn, tk, frac):
+    """Every block height of the tiled kernel: ragged M (300 rows) and N (640 = 2.5 blocks of 256)."""
+    prob = I.make_problem("bm", 300, 640, 1024, tn, tk, frac=frac, cfg=48)
+    pw = pack_problem(P, prob)
+    x = dev_u16(prob.x)
+    ref = O.gemm_ref(prob.x, O.masked_weight(prob.w, prob.mask))
+    y32 = pw.gemm(x, out_dtype=torch.float32, kernel="tiled", block_m=block_m)
+    y16 = pw.gemm(x, out_dtype=torch.bfloat16, kernel="tiled", block_m=block_m)
+    assert O.rel_error(y_host(y32), ref) <= 1e-4
+    assert O.rel_error(y_host(y16), ref) <= TOL
+
+
+@pytest.mark.parametrize("block_m", [256, 128, 64])
+def test_tiled_block_rows_one_hot_exact(P, block_m):
+    prob = I.make_problem("bmoh", 200, 256, 512, 64, 128, frac=0.7, cfg=49)
+    ks = (np.arange(200) * 37 + 11) % 512
+    x = np.zeros((200, 512), np.uint16)
+    x[np.arange(200), ks] = 0x3F80
+    pw = pack_problem(P, prob)
+    y = pw.gemm(dev_u16(x), kernel="tiled", block_m=block_m)
+    assert np.array_equal(host_u16(y), O.masked_weight(prob.w, prob.mask)[:, ks].T)
+
+
+def test_tiled_block_rows_rejects_other_values(P):
+    prob = I.make_problem("bmbad", 32, 128, 128, 64, 64, frac=0.5, cfg=50)
+    pw = pack_problem(P, prob)
+    with pytest.raises(P.PatchError) as e:
+        pw.gemm(dev_u16(prob.x), kernel="tiled", block_m=96)
+    assert e.value.status_name == "PATCH_E_INVALID_ARG"
+
+
 def test_strided_x_and_y(P):
     prob = I.make_problem("ld", 40, 256, 512, 64, 64, frac=0.5, cfg=43)
     pw = pack_problem(P, prob)
