@@ -61,7 +61,7 @@ typedef enum { PATCH_TILE_DENSE = 0, PATCH_TILE_SPARSE24 = 1 } patch_tile_type;
 typedef enum {
   PATCH_KERNEL_AUTO = 0,
   PATCH_KERNEL_TILED = 1,  /* LDS-staged MFMA tiles, for prefill-sized M */
-  PATCH_KERNEL_STREAM = 2  /* split-K weight streaming, for M <= 16 (decode) */
+  PATCH_KERNEL_STREAM = 2  /* weight streaming, one workgroup per 16 rows of W, for M <= 16 (decode) */
 } patch_kernel;
 
 typedef struct patch_weight patch_weight; /* opaque, owned by the library */
@@ -128,19 +128,18 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
  *   y      device, [m][ldy] of bf16 (round to nearest even) or fp32,
  *          ldy >= n, ldy % 8 == 0.  Written, never read.  Must not alias x.
  *
- * Never allocates and never blocks the host.  At most one patch_gemm per
- * handle may be in flight at a time (the handle's split-K workspace is
- * shared); calls on one stream are naturally ordered.
+ * Never allocates, never blocks the host and keeps no state between calls:
+ * calls on the same handle may overlap on different streams (they only read
+ * the handle).  Y is deterministic: the same inputs give the same bits.
  */
 patch_status patch_gemm(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx,
                         void* y, int64_t ldy, patch_out_dtype y_dtype, void* stream);
 
 /* patch_gemm with the kernel chosen by the caller, for tests and measurements.
- * `variant` <= 0 lets the library choose; a positive value forces
- *   PATCH_KERNEL_STREAM: the number of K slices (clamped to [1, K / 64]);
- *   PATCH_KERNEL_TILED:  the X rows per workgroup, 256, 128 or 64 (other
- *                        values: PATCH_E_INVALID_ARG);
- * and is ignored under PATCH_KERNEL_AUTO.  PATCH_KERNEL_STREAM needs m <= 16. */
+ * `variant` <= 0 lets the library choose; for PATCH_KERNEL_TILED a positive
+ * value forces the X rows per workgroup, 256, 128 or 64 (other values:
+ * PATCH_E_INVALID_ARG).  It is ignored by PATCH_KERNEL_STREAM and
+ * PATCH_KERNEL_AUTO.  PATCH_KERNEL_STREAM needs m <= 16. */
 patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx,
                                void* y, int64_t ldy, patch_out_dtype y_dtype,
                                patch_kernel kernel, int32_t variant, void* stream);

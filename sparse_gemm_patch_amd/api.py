@@ -121,12 +121,11 @@ class PackedWeight:
             _LIB.patch_destroy(h)
 
     def gemm(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
-             kernel: str = "auto", split_k: int = 0, block_m: int = 0, stream=None) -> torch.Tensor:
+             kernel: str = "auto", block_m: int = 0, stream=None) -> torch.Tensor:
         """Y = X . W_masked^T for X bf16 [m][k]; returns Y [m][n] (bf16 or fp32).
 
-        kernel "stream" takes split_k (K slices, 0 = library's choice); kernel
-        "tiled" takes block_m (X rows per workgroup: 256, 128 or 64; 0 = library's
-        choice)."""
+        kernel "tiled" takes block_m (X rows per workgroup: 256, 128 or 64; 0 =
+        the library's choice)."""
         _check_cuda(x, "x", torch.bfloat16)
         ldx = _row_major_2d(x, "x")
         if x.shape[1] != self.k:
@@ -145,7 +144,7 @@ class PackedWeight:
             raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
         st = load().patch_gemm_kernel(self._h, ctypes.c_void_p(x.data_ptr()), m, ldx, ctypes.c_void_p(out.data_ptr()),
                                       ldy, OUT_DTYPE[out_dtype], KERNEL[kernel],
-                                      int(split_k if kernel == "stream" else block_m if kernel == "tiled" else 0),
+                                      int(block_m if kernel == "tiled" else 0),
                                       _stream_handle(stream))
         if st:
             _raise(st)

@@ -111,13 +111,10 @@ void free_weight(patch_weight* w) {
   dev_free(w->dense_vals);
   dev_free(w->sparse_vals);
   dev_free(w->sparse_meta);
-  dev_free(w->ws);
-  dev_free(w->counters);
   delete w;
 }
 
 // K slices the streaming kernel may use (sizes the per-handle workspace).
-constexpr int kMaxSplits = 32;
 
 }  // namespace
 
@@ -157,7 +154,6 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
   pw->tiles_k = k / tile_k;
   pw->tiles = tiles;
   pw->last_stream = s;
-  pw->max_splits = kMaxSplits;
 
   if (tiles == 0) {
     if (info) fill_info(pw, info);
@@ -227,10 +223,8 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
 
   PATCH_TRY_ALLOC(pw->dense_vals, (size_t)pw->n_dense * tile_n * tile_k * 2);
   PATCH_TRY_ALLOC(pw->sparse_vals, (size_t)pw->n_sparse * tile_n * tile_k);
-  PATCH_TRY_ALLOC(pw->sparse_meta, (size_t)pw->n_sparse * tile_n * tile_k / 8);
-  PATCH_TRY_ALLOC(pw->ws, (size_t)kMaxSplits * 16 * n * sizeof(float));
-  PATCH_TRY_ALLOC(pw->counters, (size_t)(n / 64) * sizeof(uint32_t));
-  PATCH_TRY_HIP(launch_fill_u32(pw->counters, n / 64, 0u, s), "fill counters");
+  // +16 B: the streaming kernel reads 16 bytes at each lane's 8-byte code slot
+  PATCH_TRY_ALLOC(pw->sparse_meta, (size_t)pw->n_sparse * tile_n * tile_k / 8 + 16);
   PATCH_TRY_HIP(launch_compress(w, ldw, mask_bits, k, (int)order, tile_n, tile_k, pw->tiles_n, pw->tiles_k,
                                 pw->tile_desc, pw->dense_vals, pw->sparse_vals, pw->sparse_meta, s),
                 "compress launch");
@@ -278,7 +272,7 @@ static patch_status gemm_common(const patch_weight* w, const uint16_t* x, int64_
   } else {
     const bool stream_kernel = kernel == PATCH_KERNEL_STREAM || (kernel == PATCH_KERNEL_AUTO && m <= 16);
     const int32_t v = kernel == PATCH_KERNEL_AUTO ? 0 : variant;
-    e = stream_kernel ? launch_gemm_stream(w, x, m, ldx, y, ldy, f32, v, s)
+    e = stream_kernel ? launch_gemm_stream(w, x, m, ldx, y, ldy, f32, s)
                       : launch_gemm_tiled(w, x, m, ldx, y, ldy, f32, v, s);
   }
   if (e != hipSuccess) return hip_fail(e, "gemm launch");

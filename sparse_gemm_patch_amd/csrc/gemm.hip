@@ -58,128 +58,111 @@ __device__ __forceinline__ void store4(void* y, int64_t ldy, int64_t m, int64_t 
 }
 
 // ------------------------------------------------------------------------
-// Streaming kernel for M <= 16 (decode).  The weight is read once, so the
-// kernel is bound by HBM bandwidth; it spreads W over the whole chip with a
-// split along K.  Grid (N/64, splits), 256 threads.  Workgroup (nb, s) owns
-// rows [64 nb, 64 nb + 64) and a contiguous range of 64-wide K chunks; its four
-// waves take every fourth chunk of that range, each accumulating 64 x 16 of
-// Y^T with four 16-row blocks.  The waves are summed through LDS in a fixed
-// order; with splits > 1 each workgroup writes a partial, and the last one to
-// arrive for a row block (arrival counter) adds the partials in split order,
-// so the result does not depend on scheduling.
+// Streaming kernel for M <= 16 (decode).
+//
+// The weight is read once, so this kernel is bound by HBM bandwidth.  One
+// workgroup of 16 waves per 16-row block of W (grid N / 16): the waves take
+// every 16th 64-wide K chunk, each keeping a 16 x 16 accumulator block of
+// Y^T, and are summed through LDS in a fixed order.  No workgroup depends on
+// another (a cross-workgroup reduction would need device-scope fences, which
+// write back a whole XCD's L2 on this chip).  Per chunk a wave loads its A
+// operand (1 KiB of 2:4 values or 2 KiB of dense positions, contiguous) and the
+// 16 X rows (two 16-byte loads per lane, rows past M read as zero), BATCH
+// chunks at a time.
 // ------------------------------------------------------------------------
+namespace streamk {
+constexpr int WAVES = 16;
+constexpr int BATCH = 2;  // chunks per wave whose loads are in flight together (1, 2, 4: within 5%; 8: 2x slower)
+}  // namespace streamk
+
 template <bool F32>
-__global__ __launch_bounds__(256) void k_gemm_stream(
+__global__ __launch_bounds__(1024) void k_gemm_stream(
     const int32_t* __restrict__ tile_desc, const uint16_t* __restrict__ dense_vals,
     const uint16_t* __restrict__ sparse_vals, const uint8_t* __restrict__ sparse_meta, int tn, int tk,
     int64_t tiles_k, int64_t n, int64_t k, const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
-    void* __restrict__ y, int64_t ldy, int splits, float* __restrict__ ws, uint32_t* __restrict__ counters) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    void* __restrict__ y, int64_t ldy) {
+  using streamk::WAVES;
+  using streamk::BATCH;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4, r16 = lane & 15;
-  const int64_t nb = blockIdx.x;
-  const int s = blockIdx.y;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int64_t chunks = k >> 6;
-  const int64_t c_begin = chunks * s / splits, c_end = chunks * (s + 1) / splits;
-
-  const int64_t n0 = nb * 64;
-  const int ks = tk == 128;          // 64-wide K chunks per tile column: 1 << ks
-  const int64_t ti = n0 >> (tn == 128 ? 7 : 6);
-  const int row0 = (int)(n0 & (tn - 1));  // first row of this block inside its tile row
-  const int64_t tile_row_base = ti * tiles_k;
+  const int ks = tk == 128;                      // 64-wide K chunks per tile column: 1 << ks
+  const int ns = tn == 128 ? 7 : 6;              // log2(TN)
+  const int64_t desc_row = (n0 >> ns) * tiles_k;
+  const int blk = (int)((n0 & (tn - 1)) >> 4);   // this block's 16-row block inside its tile
+  const int bt = tn >> 4;
 
   const bool m_ok = r16 < m;
-  const uint16_t* xrow = x + (int64_t)r16 * ldx;
+  const uint16_t* xrow = x + (int64_t)(m_ok ? r16 : 0) * ldx + 8 * q;
+  const uint8_t* dbase = reinterpret_cast<const uint8_t*>(dense_vals) + lane * 16;
+  const uint8_t* sbase = reinterpret_cast<const uint8_t*>(sparse_vals) + lane * 16;
+  const uint8_t* mbase = sparse_meta + lane * 8;
 
-  f32x4 acc[4];
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // This wave's chunks are c = wave + 16 j.  Their tile descriptors arrive
+  // with one load (lane j holds chunk j's), so that the operand loads of four
+  // chunks can be issued back to back before their MFMAs.
+  for (int64_t base = wave; base < chunks; base += (int64_t)WAVES * 64) {
+    const int nj = (int)min((int64_t)64, (chunks - base + WAVES - 1) / WAVES);
+    const int64_t cl = base + (int64_t)WAVES * lane;
+    const int32_t dl = lane < nj ? tile_desc[desc_row + (cl >> ks)] : 0;
+    for (int j = 0; j < nj; j += BATCH) {
+      // BATCH chunks, past the last one clamped to it (loaded, not used): every
+      // chunk issues the same four 16-byte loads whatever its tile type, so
+      // the waits the compiler places stay exact.
+      int32_t d[BATCH];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int bt = tn >> 4;                  // 16-row blocks per tile
-  const int blk0 = row0 >> 4;              // this row block's first 16-row block in its tile
-  for (int64_t c = c_begin + wave; c < c_end; c += 4) {
-    const int64_t k0 = c << 6;
-    const bf16x8 xb0 = m_ok ? ld8(xrow + k0 + 8 * q) : zero8();
-    const bf16x8 xb1 = m_ok ? ld8(xrow + k0 + 32 + 8 * q) : zero8();
-    const bf16x16 xb = cat16(xb0, xb1);
-    const int32_t d = tile_desc[tile_row_base + (c >> ks)];
-    const int64_t slot = d >> 1;
-    const int u0 = (int)(c & ks) * bt + blk0;  // operand unit of row block b is u0 + b
-    if ((d & 1) == PATCH_TILE_DENSE) {
-      const uint8_t* wt = reinterpret_cast<const uint8_t*>(dense_vals) + (slot * tn * tk + (int64_t)u0 * 1024) * 2 + lane * 16;
-      bf16x8 a0[4], a1[4];
+      for (int t = 0; t < BATCH; ++t) d[t] = __builtin_amdgcn_readlane(dl, min(j + t, nj - 1));
+      bf16x16 xb[BATCH];
+      bf16x8 a0[BATCH];
+      u32x4 w2[BATCH];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        a0[b] = *reinterpret_cast<const bf16x8*>(wt + b * 2048);
-        a1[b] = *reinterpret_cast<const bf16x8*>(wt + b * 2048 + 1024);
+      for (int t = 0; t < BATCH; ++t) {
+        const int64_t c = base + (int64_t)WAVES * min(j + t, nj - 1);
+        xb[t] = m_ok ? cat16(ld8(xrow + (c << 6)), ld8(xrow + (c << 6) + 32)) : cat16(zero8(), zero8());
+        const int64_t slot = d[t] >> 1;
+        const int64_t u = (c & ks) * bt + blk;  // operand unit of this block and chunk
+        const bool dn = (d[t] & 1) == PATCH_TILE_DENSE;
+        const uint8_t* dw = dbase + (slot * tn * tk + u * 1024) * 2;
+        const uint8_t* sw = sbase + slot * tn * tk + u * 1024;
+        const uint8_t* cw = mbase + slot * tn * (tk >> 3) + (u >> 2) * 512;  // lane's 8 bytes of codes
+        a0[t] = *reinterpret_cast<const bf16x8*>(dn ? dw : sw);
+        w2[t] = *reinterpret_cast<const u32x4*>(dn ? dw + 1024 : cw);  // dense positions (2,3), or the codes
       }
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        acc[b] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[b], xb, acc[b], 0x4444, 0, 0);
-        acc[b] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a1[b], xb, acc[b], 0xEEEE, 0, 0);
-      }
-    } else {
-      const uint8_t* vt = reinterpret_cast<const uint8_t*>(sparse_vals) + slot * tn * tk + (int64_t)u0 * 1024 + lane * 16;
-      // codes of the four blocks: 8 bytes per lane; abid picks the 16-bit half
-      const uint2 codes = *reinterpret_cast<const uint2*>(sparse_meta + slot * tn * (tk >> 3) + (int64_t)(u0 >> 2) * 512 + lane * 8);
-      bf16x8 a[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) a[b] = *reinterpret_cast<const bf16x8*>(vt + b * 1024);
-      acc[0] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[0], xb, acc[0], (int)codes.x, 0, 0);
-      acc[1] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[1], xb, acc[1], (int)codes.x, 0, 1);
-      acc[2] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[2], xb, acc[2], (int)codes.y, 0, 0);
-      acc[3] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[3], xb, acc[3], (int)codes.y, 0, 1);
-    }
-  }
-
-  // Sum the four waves in a fixed order: red[wave][n_local][m] in LDS.
-  __shared__ float red[4][64][17];
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][16 * b + 4 * q + r][r16] = acc[b][r];
-  __syncthreads();
-
-  // Thread t handles (n_local = t / 4, m quarter = t % 4 -> m = 4*(t%4) .. +3).
-  const int nl = threadIdx.x >> 2, mq = (threadIdx.x & 3) * 4;
-  float v[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = red[0][nl][mq + j] + red[1][nl][mq + j] + red[2][nl][mq + j] + red[3][nl][mq + j];
-
-  if (splits == 1) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t mm = mq + j;
-      if (mm < m) {
-        if (F32) reinterpret_cast<float*>(y)[mm * ldy + n0 + nl] = v[j];
-        else reinterpret_cast<uint16_t*>(y)[mm * ldy + n0 + nl] = f32_to_bf16_rne(v[j]);
+      for (int t = 0; t < BATCH; ++t) {
+        if (j + t >= nj) continue;
+        const int64_t c = base + (int64_t)WAVES * (j + t);
+        const int ub = (int)(((c & ks) * bt + blk) & 3);  // block within its 4-block code group
+        if ((d[t] & 1) == PATCH_TILE_DENSE) {
+          acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[t], xb[t], acc, 0x4444, 0, 0);
+          acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, w2[t]), xb[t], acc, 0xEEEE, 0, 0);
+        } else {
+          const uint32_t word = ub < 2 ? w2[t].x : w2[t].y;  // codes of blocks (0,1) or (2,3)
+          acc = ub & 1 ? __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[t], xb[t], acc, (int)word, 0, 1)
+                       : __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[t], xb[t], acc, (int)word, 0, 0);
+        }
       }
     }
-    return;
   }
 
-  // ws layout [split][16][n]; only rows m < M are written and read.
+  // Sum the waves in a fixed order: lane holds rows 4 q + i of column m = r16.
+  __shared__ float red[WAVES][16][17];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t mm = mq + j;
-    if (mm < m) ws[((int64_t)s * 16 + mm) * n + n0 + nl] = v[j];
-  }
-  __threadfence();
+  for (int i = 0; i < 4; ++i) red[wave][4 * q + i][r16] = acc[i];
   __syncthreads();
-  __shared__ uint32_t s_last;
-  if (threadIdx.x == 0) s_last = (atomicAdd(&counters[nb], 1u) == (uint32_t)(splits - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  if (threadIdx.x < 256) {
+    const int nl = threadIdx.x >> 4, mm = threadIdx.x & 15;
+    float v = 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t mm = mq + j;
-    if (mm >= m) continue;
-    float acc_s = 0.f;
-    for (int t = 0; t < splits; ++t) acc_s += __builtin_nontemporal_load(&ws[((int64_t)t * 16 + mm) * n + n0 + nl]);
-    if (F32) reinterpret_cast<float*>(y)[mm * ldy + n0 + nl] = acc_s;
-    else reinterpret_cast<uint16_t*>(y)[mm * ldy + n0 + nl] = f32_to_bf16_rne(acc_s);
+    for (int w = 0; w < WAVES; ++w) v += red[w][nl][mm];
+    if (mm < m) {
+      if (F32) reinterpret_cast<float*>(y)[mm * ldy + n0 + nl] = v;
+      else reinterpret_cast<uint16_t*>(y)[mm * ldy + n0 + nl] = f32_to_bf16_rne(v);
+    }
   }
-  if (threadIdx.x == 0) counters[nb] = 0;  // ready for the next call on this handle
 }
 
 // ------------------------------------------------------------------------
@@ -446,34 +429,16 @@ __global__ void k_fill_zero_y(void* y, int64_t m, int64_t n, int64_t ldy) {
 
 }  // namespace
 
-int stream_default_splits(const patch_weight* pw, int64_t m) {
-  (void)m;
-  const int64_t nblocks = pw->n / 64;
-  const int64_t chunks = pw->k / 64;
-  int64_t splits = (1024 + nblocks - 1) / nblocks;  // aim at ~1024 workgroups
-  const int64_t max_by_k = chunks / 4 > 0 ? chunks / 4 : 1;  // keep >= 1 chunk per wave
-  if (splits > max_by_k) splits = max_by_k;
-  if (splits > pw->max_splits) splits = pw->max_splits;
-  if (splits < 1) splits = 1;
-  return (int)splits;
-}
-
 hipError_t launch_gemm_stream(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx, void* y,
-                              int64_t ldy, int out_f32, int split_k, hipStream_t s) {
-  const int64_t chunks = pw->k / 64;
-  int splits = split_k > 0 ? split_k : stream_default_splits(pw, m);
-  if (splits > chunks) splits = (int)chunks;
-  if (splits > pw->max_splits) splits = pw->max_splits;
-  if (splits < 1) splits = 1;
-  dim3 grid((unsigned)(pw->n / 64), (unsigned)splits);
+                              int64_t ldy, int out_f32, hipStream_t s) {
+  const dim3 grid((unsigned)(pw->n / 16));
+  const dim3 block(64 * streamk::WAVES);
   if (out_f32)
-    hipLaunchKernelGGL(k_gemm_stream<true>, grid, dim3(256), 0, s, pw->tile_desc, pw->dense_vals, pw->sparse_vals,
-                       pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x, m, ldx, y, ldy, splits, pw->ws,
-                       pw->counters);
+    hipLaunchKernelGGL(k_gemm_stream<true>, grid, block, 0, s, pw->tile_desc, pw->dense_vals, pw->sparse_vals,
+                       pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x, m, ldx, y, ldy);
   else
-    hipLaunchKernelGGL(k_gemm_stream<false>, grid, dim3(256), 0, s, pw->tile_desc, pw->dense_vals,
-                       pw->sparse_vals, pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x, m, ldx, y,
-                       ldy, splits, pw->ws, pw->counters);
+    hipLaunchKernelGGL(k_gemm_stream<false>, grid, block, 0, s, pw->tile_desc, pw->dense_vals, pw->sparse_vals,
+                       pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x, m, ldx, y, ldy);
   return hipGetLastError();
 }
 

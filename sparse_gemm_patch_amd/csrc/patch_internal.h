@@ -23,10 +23,6 @@ struct patch_weight {
   uint16_t* dense_vals;  // [D][TN][TK]
   uint16_t* sparse_vals; // [S][TN][TK/2]
   uint8_t* sparse_meta;  // [S][TN][TK/8]
-  // split-K workspace of the streaming kernel
-  float* ws;             // [max_splits][16][n] fp32 partial sums
-  uint32_t* counters;    // [n / 64] arrival counters, zero between calls
-  int32_t max_splits;
   hipStream_t last_stream;
 };
 
@@ -53,14 +49,12 @@ hipError_t launch_mask_unpack(const uint8_t* bits, int64_t count, int order, uin
 
 // ---- GEMM kernels ----
 hipError_t launch_gemm_stream(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx,
-                              void* y, int64_t ldy, int out_f32, int split_k, hipStream_t s);
+                              void* y, int64_t ldy, int out_f32, hipStream_t s);
 // block_m: X rows per workgroup (256, 128 or 64); 0 lets tiled_block_m choose.
 hipError_t launch_gemm_tiled(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx,
                              void* y, int64_t ldy, int out_f32, int block_m, hipStream_t s);
 int tiled_block_m(int64_t n, int64_t m);
 hipError_t launch_fill_zero_y(void* y, int64_t m, int64_t n, int64_t ldy, int out_f32, hipStream_t s);
-// Split count the streaming kernel uses when the caller does not force one.
-int stream_default_splits(const patch_weight* pw, int64_t m);
 
 // ---- device helpers ----
 // fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.

@@ -146,7 +146,7 @@ def test_shape_and_argument_errors(P):
 def test_allocation_failure_is_clean(P, monkeypatch):
     prob = I.make_problem("nomem", 1, 256, 256, 64, 64, frac=0.5, cfg=24)
     w, bits = dev_u16(prob.w), dev_u8(prob.bits)
-    for nth in (1, 2, 3, 4, 6, 8):
+    for nth in (1, 2, 3, 4, 5, 6):  # scratch, tile map, descriptors, dense, 2:4 values, codes
         monkeypatch.setenv("PATCH_TEST_FAIL_ALLOC", str(nth))
         with pytest.raises(P.PatchError) as e:
             P.pack(w, bits, tile=(64, 64))
@@ -168,9 +168,9 @@ def test_empty_weights(P):
 
 # ------------------------------------------------------------------ GEMM parity
 
-def gemm_case(P, prob, kernel="auto", out_dtype=torch.bfloat16, split_k=0):
+def gemm_case(P, prob, kernel="auto", out_dtype=torch.bfloat16):
     pw = pack_problem(P, prob)
-    y = pw.gemm(dev_u16(prob.x), out_dtype=out_dtype, kernel=kernel, split_k=split_k)
+    y = pw.gemm(dev_u16(prob.x), out_dtype=out_dtype, kernel=kernel)
     torch.cuda.synchronize()
     wm = O.masked_weight(prob.w, prob.mask)
     ref = O.gemm_ref(prob.x, wm)
@@ -221,17 +221,19 @@ def test_ones_count_kept_exactly(P, kernel, m):
     assert np.array_equal(y_host(y), np.broadcast_to(want, (m, 256)))
 
 
-@pytest.mark.parametrize("split_k", [1, 2, 3, 5, 8, 32])
-def test_stream_split_k_and_determinism(P, split_k):
-    prob = I.make_problem("sk", 16, 512, 2048, 128, 128, frac=0.5, cfg=42)
+@pytest.mark.parametrize("k", [64, 192, 1088, 2048])
+@pytest.mark.parametrize("m", [1, 5, 16])
+def test_stream_k_ranges_and_determinism(P, k, m):
+    """16 waves share the K chunks of a block: fewer chunks than waves, a ragged last round, many rounds."""
+    prob = I.make_problem("sk", m, 512, k, 128, 64, frac=0.5, cfg=42)
     pw = pack_problem(P, prob)
     x = dev_u16(prob.x)
-    y1 = pw.gemm(x, out_dtype=torch.float32, kernel="stream", split_k=split_k)
-    y2 = pw.gemm(x, out_dtype=torch.float32, kernel="stream", split_k=split_k)
+    y1 = pw.gemm(x, out_dtype=torch.float32, kernel="stream")
+    y2 = pw.gemm(x, out_dtype=torch.float32, kernel="stream")
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)  # bitwise run-to-run
     ref = O.gemm_ref(prob.x, O.masked_weight(prob.w, prob.mask))
-    assert O.rel_error(y_host(y1), ref) <= TOL
+    assert O.rel_error(y_host(y1), ref) <= 1e-4
 
 
 @pytest.mark.parametrize("block_m", [256, 128, 64])
