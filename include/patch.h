@@ -145,6 +145,44 @@ patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t
                                patch_kernel kernel, int32_t variant, void* stream);
 
 /*
+ * patch_gemm_grouped -- several independent linear layers in one launch.
+ *
+ * A transformer layer applies several linears to the same or to different
+ * inputs (the card's model is LLaMA-3.2-1B: q, k, v, o, gate, up and down
+ * projections per layer, each with its own PATCH mask).  Each item is the
+ * patch_gemm of its own handle, X and Y; the whole group runs as at most one
+ * launch of each kernel (STREAM for the items with m <= 16, TILED for the
+ * rest) plus a zero fill per item with K = 0, so small projections share the
+ * chip instead of running one after another.
+ *
+ *   items    host, `count` items; read during the call only.
+ *   count    0 .. 16 (0 is a no-op).
+ *   y_dtype  applies to every item.
+ *
+ * Each item obeys patch_gemm's rules (the first failing item is named in the
+ * message, and nothing is launched).  The Y buffers must not overlap one
+ * another or any X of the group; X buffers and handles may be shared.  Each
+ * item's Y equals, bit for bit, what patch_gemm gives for it alone.  Never
+ * allocates and never blocks the host.
+ */
+typedef struct {
+  const patch_weight* w;
+  const uint16_t* x; /* device, bf16 [m][ldx] */
+  int64_t m;
+  int64_t ldx;
+  void* y;           /* device, [m][ldy] of y_dtype */
+  int64_t ldy;
+} patch_gemm_item;
+
+patch_status patch_gemm_grouped(const patch_gemm_item* items, int32_t count, patch_out_dtype y_dtype,
+                                void* stream);
+
+/* patch_gemm_grouped with the kernel chosen by the caller (`kernel` and
+ * `variant` as in patch_gemm_kernel, applied to every item). */
+patch_status patch_gemm_grouped_kernel(const patch_gemm_item* items, int32_t count, patch_out_dtype y_dtype,
+                                       patch_kernel kernel, int32_t variant, void* stream);
+
+/*
  * patch_unpack -- rebuild the masked dense weight: the card's "apply the mask"
  * (pruned weights zeroed).  Kept weights get their bf16 bits back exactly;
  * pruned ones get +0.0 (0x0000).

@@ -23,8 +23,10 @@ OUT_DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 DENSE, SPARSE24 = 0, 1
 
 # Exported entry points; kept in step with include/patch.h.
-SYMBOLS = ("patch_pack", "patch_gemm", "patch_gemm_kernel", "patch_unpack", "patch_mask_unpack",
-           "patch_get_info", "patch_export", "patch_destroy", "patch_last_error")
+SYMBOLS = ("patch_pack", "patch_gemm", "patch_gemm_kernel", "patch_gemm_grouped", "patch_gemm_grouped_kernel",
+           "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_destroy",
+           "patch_last_error")
+MAX_GROUP = 16
 
 
 class PatchInfo(ctypes.Structure):
@@ -37,6 +39,11 @@ class PatchInfo(ctypes.Structure):
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class GemmItem(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("x", ctypes.c_void_p), ("m", ctypes.c_int64), ("ldx", ctypes.c_int64),
+                ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
 
 
 class PatchError(RuntimeError):
@@ -68,6 +75,8 @@ def load() -> ctypes.CDLL:
                              ctypes.POINTER(PatchInfo)]
     L.patch_gemm.argtypes = [vp, vp, i64, i64, vp, i64, ctypes.c_int, vp]
     L.patch_gemm_kernel.argtypes = [vp, vp, i64, i64, vp, i64, ctypes.c_int, ctypes.c_int, i32, vp]
+    L.patch_gemm_grouped.argtypes = [ctypes.POINTER(GemmItem), i32, ctypes.c_int, vp]
+    L.patch_gemm_grouped_kernel.argtypes = [ctypes.POINTER(GemmItem), i32, ctypes.c_int, ctypes.c_int, i32, vp]
     L.patch_unpack.argtypes = [vp, vp, i64, vp]
     L.patch_mask_unpack.argtypes = [vp, i64, ctypes.c_int, vp, vp]
     L.patch_get_info.argtypes = [vp, ctypes.POINTER(PatchInfo)]
@@ -76,8 +85,8 @@ def load() -> ctypes.CDLL:
     L.patch_destroy.restype = None
     L.patch_last_error.argtypes = []
     L.patch_last_error.restype = ctypes.c_char_p
-    for name in ("patch_pack", "patch_gemm", "patch_gemm_kernel", "patch_unpack", "patch_mask_unpack",
-                 "patch_get_info", "patch_export"):
+    for name in ("patch_pack", "patch_gemm", "patch_gemm_kernel", "patch_gemm_grouped", "patch_gemm_grouped_kernel",
+                 "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L
@@ -120,16 +129,14 @@ class PackedWeight:
         if h and _LIB is not None:
             _LIB.patch_destroy(h)
 
-    def gemm(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
-             kernel: str = "auto", block_m: int = 0, stream=None) -> torch.Tensor:
-        """Y = X . W_masked^T for X bf16 [m][k]; returns Y [m][n] (bf16 or fp32).
-
-        kernel "tiled" takes block_m (X rows per workgroup: 256, 128 or 64; 0 =
-        the library's choice)."""
+    def _operands(self, x: torch.Tensor, out: Optional[torch.Tensor], out_dtype: torch.dtype):
+        """Checks X, allocates or checks Y; returns (m, ldx, out, ldy)."""
         _check_cuda(x, "x", torch.bfloat16)
         ldx = _row_major_2d(x, "x")
         if x.shape[1] != self.k:
             raise ValueError(f"x has {x.shape[1]} columns, weight has k = {self.k}")
+        if out_dtype not in OUT_DTYPE:
+            raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
         m = x.shape[0]
         if out is None:
             ldy = (self.n + 7) // 8 * 8
@@ -139,9 +146,15 @@ class PackedWeight:
             _check_cuda(out, "out", out_dtype)
             if tuple(out.shape) != (m, self.n):
                 raise ValueError(f"out must be [{m}][{self.n}]")
-        ldy = _row_major_2d(out, "out")
-        if out_dtype not in OUT_DTYPE:
-            raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+        return m, ldx, out, _row_major_2d(out, "out")
+
+    def gemm(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+             kernel: str = "auto", block_m: int = 0, stream=None) -> torch.Tensor:
+        """Y = X . W_masked^T for X bf16 [m][k]; returns Y [m][n] (bf16 or fp32).
+
+        kernel "tiled" takes block_m (X rows per workgroup: 256, 128 or 64; 0 =
+        the library's choice)."""
+        m, ldx, out, ldy = self._operands(x, out, out_dtype)
         st = load().patch_gemm_kernel(self._h, ctypes.c_void_p(x.data_ptr()), m, ldx, ctypes.c_void_p(out.data_ptr()),
                                       ldy, OUT_DTYPE[out_dtype], KERNEL[kernel],
                                       int(block_m if kernel == "tiled" else 0),
@@ -176,6 +189,31 @@ class PackedWeight:
         if st:
             _raise(st)
         return arrs
+
+
+def gemm_grouped(products, outs=None, out_dtype: torch.dtype = torch.bfloat16, kernel: str = "auto",
+                 block_m: int = 0, stream=None) -> list:
+    """Several independent products in one launch per kernel.
+
+    products: sequence of (PackedWeight, X) pairs (at most 16); outs: None or a
+    matching sequence of Y tensors / None.  Returns the Y list; each Y equals
+    what PackedWeight.gemm gives for its pair alone, bit for bit."""
+    products = list(products)
+    if len(products) > MAX_GROUP:
+        raise ValueError(f"at most {MAX_GROUP} products per group, got {len(products)}")
+    outs = [None] * len(products) if outs is None else list(outs)
+    if len(outs) != len(products):
+        raise ValueError("outs must match products")
+    items = (GemmItem * max(len(products), 1))()
+    for i, ((pw, x), out) in enumerate(zip(products, outs)):
+        m, ldx, out, ldy = pw._operands(x, out, out_dtype)
+        outs[i] = out
+        items[i] = GemmItem(pw._h, x.data_ptr(), m, ldx, out.data_ptr(), ldy)
+    st = load().patch_gemm_grouped_kernel(items, len(products), OUT_DTYPE[out_dtype], KERNEL[kernel],
+                                          int(block_m if kernel == "tiled" else 0), _stream_handle(stream))
+    if st:
+        _raise(st)
+    return outs
 
 
 def pack(w: torch.Tensor, bits: torch.Tensor, tile=(128, 128), bit_order: str = "big",

@@ -114,8 +114,6 @@ void free_weight(patch_weight* w) {
   delete w;
 }
 
-// K slices the streaming kernel may use (sizes the per-handle workspace).
-
 }  // namespace
 
 extern "C" {
@@ -238,20 +236,17 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
   return ok();
 }
 
-static patch_status gemm_common(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y,
-                                int64_t ldy, patch_out_dtype y_dtype, patch_kernel kernel, int32_t variant,
-                                void* stream) {
+// Checks one product's arguments; sets *skip when it has nothing to compute
+// (m = 0 or n = 0).
+static patch_status check_product(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y,
+                                  int64_t ldy, bool* skip) {
+  *skip = false;
   if (!w) return fail(PATCH_E_INVALID_ARG, "weight handle is NULL");
-  if (y_dtype != PATCH_OUT_BF16 && y_dtype != PATCH_OUT_F32)
-    return fail(PATCH_E_INVALID_ARG, "bad output dtype %d", (int)y_dtype);
-  if (kernel != PATCH_KERNEL_AUTO && kernel != PATCH_KERNEL_TILED && kernel != PATCH_KERNEL_STREAM)
-    return fail(PATCH_E_INVALID_ARG, "bad kernel %d", (int)kernel);
   if (m < 0) return fail(PATCH_E_INVALID_ARG, "m = %lld < 0", (long long)m);
-  if (kernel == PATCH_KERNEL_STREAM && m > 16)
-    return fail(PATCH_E_INVALID_ARG, "the streaming kernel takes m <= 16, got %lld", (long long)m);
-  if (kernel == PATCH_KERNEL_TILED && variant > 0 && variant != 256 && variant != 128 && variant != 64)
-    return fail(PATCH_E_INVALID_ARG, "tiled block rows must be 256, 128 or 64, got %d", (int)variant);
-  if (m == 0 || w->n == 0) return ok();
+  if (m == 0 || w->n == 0) {
+    *skip = true;
+    return ok();
+  }
   if (!y) return fail(PATCH_E_INVALID_ARG, "y is NULL");
   if (!aligned16(y)) return fail(PATCH_E_INVALID_ARG, "y must be 16-byte aligned");
   if (ldy < w->n || ldy % 8) return fail(PATCH_E_INVALID_ARG, "ldy %lld must be >= n and a multiple of 8", (long long)ldy);
@@ -260,34 +255,91 @@ static patch_status gemm_common(const patch_weight* w, const uint16_t* x, int64_
     if (!aligned16(x)) return fail(PATCH_E_INVALID_ARG, "x must be 16-byte aligned");
     if (ldx < w->k || ldx % 8) return fail(PATCH_E_INVALID_ARG, "ldx %lld must be >= k and a multiple of 8", (long long)ldx);
   }
+  return ok();
+}
+
+// Runs up to PATCH_MAX_GROUP products: those with K = 0 get a zero fill, the
+// rest one launch of the streaming kernel (m <= 16) and/or one of the tiled
+// kernel.  kernel / variant as in patch_gemm_kernel.
+static patch_status gemm_group_common(const patch_gemm_item* items, int32_t count, patch_out_dtype y_dtype,
+                                      patch_kernel kernel, int32_t variant, void* stream) {
+  if (count < 0 || count > PATCH_MAX_GROUP)
+    return fail(PATCH_E_INVALID_ARG, "group of %d products, must be 0..%d", (int)count, PATCH_MAX_GROUP);
+  if (count > 0 && !items) return fail(PATCH_E_INVALID_ARG, "items is NULL");
+  if (y_dtype != PATCH_OUT_BF16 && y_dtype != PATCH_OUT_F32)
+    return fail(PATCH_E_INVALID_ARG, "bad output dtype %d", (int)y_dtype);
+  if (kernel != PATCH_KERNEL_AUTO && kernel != PATCH_KERNEL_TILED && kernel != PATCH_KERNEL_STREAM)
+    return fail(PATCH_E_INVALID_ARG, "bad kernel %d", (int)kernel);
+  if (kernel == PATCH_KERNEL_TILED && variant > 0 && variant != 256 && variant != 128 && variant != 64)
+    return fail(PATCH_E_INVALID_ARG, "tiled block rows must be 256, 128 or 64, got %d", (int)variant);
+  if (count == 0) return ok();
+  bool skip[PATCH_MAX_GROUP];
+  for (int i = 0; i < count; ++i) {
+    const patch_gemm_item& it = items[i];
+    const patch_status st = check_product(it.w, it.x, it.m, it.ldx, it.y, it.ldy, &skip[i]);
+    if (st != PATCH_OK) {
+      if (count == 1) return st;
+      const std::string msg = g_err;  // fail() rewrites g_err
+      return fail(st, "product %d: %s", i, msg.c_str());
+    }
+    if (kernel == PATCH_KERNEL_STREAM && it.m > 16)
+      return fail(PATCH_E_INVALID_ARG, "the streaming kernel takes m <= 16, got %lld", (long long)it.m);
+  }
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev != w->device) return fail(PATCH_E_INVALID_ARG, "weight lives on device %d, current device is %d", w->device, dev);
+  for (int i = 0; i < count; ++i)
+    if (!skip[i] && items[i].w->device != dev)
+      return fail(PATCH_E_INVALID_ARG, "product %d: weight lives on device %d, current device is %d", i,
+                  items[i].w->device, dev);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const_cast<patch_weight*>(w)->last_stream = s;
   const int f32 = y_dtype == PATCH_OUT_F32;
-  if (w->k == 0) {
-    e = launch_fill_zero_y(y, m, w->n, ldy, f32, s);
-  } else {
-    const bool stream_kernel = kernel == PATCH_KERNEL_STREAM || (kernel == PATCH_KERNEL_AUTO && m <= 16);
-    const int32_t v = kernel == PATCH_KERNEL_AUTO ? 0 : variant;
-    e = stream_kernel ? launch_gemm_stream(w, x, m, ldx, y, ldy, f32, s)
-                      : launch_gemm_tiled(w, x, m, ldx, y, ldy, f32, v, s);
+  gemm_group streamed = {}, tiled = {};
+  for (int i = 0; i < count; ++i) {
+    if (skip[i]) continue;
+    const patch_gemm_item& it = items[i];
+    const_cast<patch_weight*>(it.w)->last_stream = s;
+    if (it.w->k == 0) {
+      e = launch_fill_zero_y(it.y, it.m, it.w->n, it.ldy, f32, s);
+      if (e != hipSuccess) return hip_fail(e, "zero-fill launch");
+      continue;
+    }
+    const bool st = kernel == PATCH_KERNEL_STREAM || (kernel == PATCH_KERNEL_AUTO && it.m <= 16);
+    gemm_group& g = st ? streamed : tiled;
+    g.p[g.count++] = make_problem(it.w, it.x, it.m, it.ldx, it.y, it.ldy);
   }
-  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  if (streamed.count) {
+    e = launch_stream_group(streamed, f32, s);
+    if (e != hipSuccess) return hip_fail(e, "gemm launch (streaming kernel)");
+  }
+  if (tiled.count) {
+    e = launch_tiled_group(tiled, f32, kernel == PATCH_KERNEL_AUTO ? 0 : variant, s);
+    if (e != hipSuccess) return hip_fail(e, "gemm launch (tiled kernel)");
+  }
   return ok();
 }
 
 patch_status patch_gemm(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y, int64_t ldy,
                         patch_out_dtype y_dtype, void* stream) {
-  return gemm_common(w, x, m, ldx, y, ldy, y_dtype, PATCH_KERNEL_AUTO, 0, stream);
+  const patch_gemm_item it = {w, x, m, ldx, y, ldy};
+  return gemm_group_common(&it, 1, y_dtype, PATCH_KERNEL_AUTO, 0, stream);
 }
 
 patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y,
                                int64_t ldy, patch_out_dtype y_dtype, patch_kernel kernel, int32_t variant,
                                void* stream) {
-  return gemm_common(w, x, m, ldx, y, ldy, y_dtype, kernel, variant, stream);
+  const patch_gemm_item it = {w, x, m, ldx, y, ldy};
+  return gemm_group_common(&it, 1, y_dtype, kernel, variant, stream);
+}
+
+patch_status patch_gemm_grouped(const patch_gemm_item* items, int32_t count, patch_out_dtype y_dtype,
+                                void* stream) {
+  return gemm_group_common(items, count, y_dtype, PATCH_KERNEL_AUTO, 0, stream);
+}
+
+patch_status patch_gemm_grouped_kernel(const patch_gemm_item* items, int32_t count, patch_out_dtype y_dtype,
+                                       patch_kernel kernel, int32_t variant, void* stream) {
+  return gemm_group_common(items, count, y_dtype, kernel, variant, stream);
 }
 
 patch_status patch_unpack(const patch_weight* w, uint16_t* w_out, int64_t ldw, void* stream) {

@@ -75,18 +75,39 @@ constexpr int WAVES = 16;
 constexpr int BATCH = 2;  // chunks per wave whose loads are in flight together (1, 2, 4: within 5%; 8: 2x slower)
 }  // namespace streamk
 
+// The product a workgroup belongs to (a short scalar scan over the group) and
+// the workgroup's index inside it; -1 for padding.
+__device__ __forceinline__ int find_problem(const gemm_group& g, int bid, int& local) {
+  for (int i = 0; i < g.count; ++i) {
+    const int b0 = g.p[i].block0;
+    if (bid >= b0 && bid < b0 + g.p[i].blocks) {
+      local = bid - b0;
+      return i;
+    }
+  }
+  return -1;
+}
+
 template <bool F32>
-__global__ __launch_bounds__(1024) void k_gemm_stream(
-    const int32_t* __restrict__ tile_desc, const uint16_t* __restrict__ dense_vals,
-    const uint16_t* __restrict__ sparse_vals, const uint8_t* __restrict__ sparse_meta, int tn, int tk,
-    int64_t tiles_k, int64_t n, int64_t k, const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
-    void* __restrict__ y, int64_t ldy) {
+__global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
   using streamk::WAVES;
   using streamk::BATCH;
+  int local;
+  const int pi = find_problem(g, blockIdx.x, local);
+  if (pi < 0) return;
+  const gemm_problem& P = g.p[pi];
+  const int32_t* __restrict__ tile_desc = P.tile_desc;
+  const uint16_t* __restrict__ dense_vals = P.dense_vals;
+  const uint16_t* __restrict__ sparse_vals = P.sparse_vals;
+  const uint8_t* __restrict__ sparse_meta = P.sparse_meta;
+  const int tn = P.tn, tk = P.tk;
+  const int64_t tiles_k = P.tiles_k, k = P.k, m = P.m, ldx = P.ldx, ldy = P.ldy;
+  const uint16_t* __restrict__ x = P.x;
+  void* __restrict__ y = P.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4, r16 = lane & 15;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n0 = (int64_t)local * 16;
   const int64_t chunks = k >> 6;
   const int ks = tk == 128;                      // 64-wide K chunks per tile column: 1 << ks
   const int ns = tn == 128 ? 7 : 6;              // log2(TN)
@@ -237,12 +258,13 @@ __device__ __forceinline__ int xswz(int r) { return r & 7; }
 // in groups of GROUP_N block columns (m fastest inside a group), makes the
 // workgroups resident on one XCD cover a compact region and share their W and
 // X in that XCD's L2.
+// bid: the workgroup's index inside its product, whose first workgroup is a
+// multiple of 8 in the launch (so bid % 8 is still its XCD).
 template <int BM>
-__device__ __forceinline__ void block_origin(int64_t n, int64_t m, int64_t& n0, int64_t& m0) {
+__device__ __forceinline__ void block_origin(int64_t n, int64_t m, int bid, int64_t& n0, int64_t& m0) {
   using namespace tiled;
   const int nbn = (int)((n + BN - 1) / BN), nbm = (int)((m + BM - 1) / BM);
   const int total = nbn * nbm;
-  const int bid = blockIdx.x;
   const int xcd = bid & 7, local = bid >> 3, base = total >> 3, rem = total & 7;
   const int id = xcd < rem ? xcd * (base + 1) + local : rem * (base + 1) + (xcd - rem) * base + local;
   const int per_group = GROUP_N * nbm;
@@ -253,13 +275,27 @@ __device__ __forceinline__ void block_origin(int64_t n, int64_t m, int64_t& n0, 
   m0 = (int64_t)(in_group / width) * BM;
 }
 
+// Tile descriptors seen through the constant address space: nothing writes the
+// packed weight while a GEMM runs, and saying so lets the wave-uniform reads go
+// through the scalar cache (a pointer taken from a kernel-argument array is
+// otherwise assumed to alias Y, which forces vector loads).
+typedef const __attribute__((address_space(4))) int32_t* const_desc_ptr;
+
 template <bool F32, int BM>
-__global__ __launch_bounds__(512, 1) void k_gemm_tiled(
-    const int32_t* __restrict__ tile_desc, const uint16_t* __restrict__ dense_vals,
-    const uint16_t* __restrict__ sparse_vals, const uint8_t* __restrict__ sparse_meta, int tn, int tk,
-    int64_t tiles_k, int64_t n, int64_t k, const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
-    void* __restrict__ y, int64_t ldy) {
+__global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
   using namespace tiled;
+  int local;
+  const int pi = find_problem(g, blockIdx.x, local);
+  if (pi < 0) return;
+  const gemm_problem& P = g.p[pi];
+  const const_desc_ptr tile_desc = (const_desc_ptr)P.tile_desc;
+  const uint16_t* __restrict__ dense_vals = P.dense_vals;
+  const uint16_t* __restrict__ sparse_vals = P.sparse_vals;
+  const uint8_t* __restrict__ sparse_meta = P.sparse_meta;
+  const int tn = P.tn, tk = P.tk;
+  const int64_t tiles_k = P.tiles_k, n = P.n, k = P.k, m = P.m, ldx = P.ldx, ldy = P.ldy;
+  const uint16_t* __restrict__ x = P.x;
+  void* __restrict__ y = P.y;
   constexpr int XB = BM / 64;                        // X blocks of 16 rows per wave
   constexpr int X_BYTES = x_bytes<BM>(), STAGE_BYTES = stage_bytes<BM>();
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -270,7 +306,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(
   const int wn = wave >> 2, wm = wave & 3;
   const int q = lane >> 4, r16 = lane & 15;
   int64_t n0, m0;
-  block_origin<BM>(n, m, n0, m0);
+  block_origin<BM>(n, m, local, n0, m0);
   const int nsteps = (int)(k / BK);
   const int ks = tk == 128;           // 64-wide K steps per tile column: 1 << ks
   const int ns = tn == 128 ? 7 : 6;   // log2(TN)
@@ -429,23 +465,42 @@ __global__ void k_fill_zero_y(void* y, int64_t m, int64_t n, int64_t ldy) {
 
 }  // namespace
 
-hipError_t launch_gemm_stream(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx, void* y,
-                              int64_t ldy, int out_f32, hipStream_t s) {
-  const dim3 grid((unsigned)(pw->n / 16));
+gemm_problem make_problem(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y, int64_t ldy) {
+  gemm_problem p = {};
+  p.tile_desc = w->tile_desc;
+  p.dense_vals = w->dense_vals;
+  p.sparse_vals = w->sparse_vals;
+  p.sparse_meta = w->sparse_meta;
+  p.x = x;
+  p.y = y;
+  p.tiles_k = w->tiles_k;
+  p.n = w->n;
+  p.k = w->k;
+  p.m = m;
+  p.ldx = ldx;
+  p.ldy = ldy;
+  p.tn = w->tn;
+  p.tk = w->tk;
+  return p;
+}
+
+hipError_t launch_stream_group(gemm_group& g, int out_f32, hipStream_t s) {
+  int64_t total = 0;
+  for (int i = 0; i < g.count; ++i) {
+    g.p[i].block0 = (int32_t)total;
+    g.p[i].blocks = (int32_t)(g.p[i].n / 16);
+    total += g.p[i].blocks;
+  }
+  if (total == 0) return hipSuccess;
   const dim3 block(64 * streamk::WAVES);
-  if (out_f32)
-    hipLaunchKernelGGL(k_gemm_stream<true>, grid, block, 0, s, pw->tile_desc, pw->dense_vals, pw->sparse_vals,
-                       pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x, m, ldx, y, ldy);
-  else
-    hipLaunchKernelGGL(k_gemm_stream<false>, grid, block, 0, s, pw->tile_desc, pw->dense_vals, pw->sparse_vals,
-                       pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x, m, ldx, y, ldy);
+  if (out_f32) hipLaunchKernelGGL(k_gemm_stream<true>, dim3((unsigned)total), block, 0, s, g);
+  else hipLaunchKernelGGL(k_gemm_stream<false>, dim3((unsigned)total), block, 0, s, g);
   return hipGetLastError();
 }
 
 namespace {
 template <bool F32, int BM>
-hipError_t launch_tiled_bm(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx, void* y, int64_t ldy,
-                           hipStream_t s) {
+hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
   constexpr int lds_bytes = tiled::STAGES * tiled::stage_bytes<BM>();  // above 64 KiB: opt in, once
   static bool attr_set = false;
   if (!attr_set) {
@@ -454,44 +509,70 @@ hipError_t launch_tiled_bm(const patch_weight* pw, const uint16_t* x, int64_t m,
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t blocks = ((pw->n + tiled::BN - 1) / tiled::BN) * ((m + BM - 1) / BM);
-  hipLaunchKernelGGL((k_gemm_tiled<F32, BM>), dim3((unsigned)blocks), dim3(512), lds_bytes, s, pw->tile_desc,
-                     pw->dense_vals, pw->sparse_vals, pw->sparse_meta, pw->tn, pw->tk, pw->tiles_k, pw->n, pw->k, x,
-                     m, ldx, y, ldy);
+  // Each product's workgroups start at a multiple of 8 (the XCD count), so the
+  // block order inside it stays XCD-aware; the padding workgroups exit at once.
+  int64_t total = 0;
+  for (int i = 0; i < g.count; ++i) {
+    g.p[i].block0 = (int32_t)total;
+    g.p[i].blocks = (int32_t)(((g.p[i].n + tiled::BN - 1) / tiled::BN) * ((g.p[i].m + BM - 1) / BM));
+    total += (g.p[i].blocks + 7) / 8 * 8;
+  }
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm_tiled<F32, BM>), dim3((unsigned)total), dim3(512), lds_bytes, s, g);
   return hipGetLastError();
+}
+
+// Relative cost of one workgroup: block height over its measured efficiency
+// (smaller blocks move more LDS bytes per flop), times the K steps.
+double block_cost(int bm, int64_t k) {
+  const double eff = bm == 256 ? 1.0 : bm == 128 ? 0.69 : 0.42;  // measured on the LLaMA-3.2-1B projections
+  return bm / 256.0 / eff * (double)(k / 64);
 }
 }  // namespace
 
-int tiled_block_m(int64_t n, int64_t m) {
-  // Estimated time ~ rounds of 256 workgroups x the block's cost, where a
-  // block of BM rows costs BM / 256 of a full one divided by its relative
-  // efficiency (smaller blocks move more LDS bytes per flop).
+int tiled_block_m(const gemm_group& g) {
+  // Estimated time of each block height: rounds of 256 workgroups when every
+  // product has the same K, else total cost spread over the CUs but never less
+  // than the longest workgroup.
   const int bms[3] = {256, 128, 64};
-  const double eff[3] = {1.0, 0.69, 0.42};  // measured on the LLaMA-3.2-1B projections
-  const int64_t nbn = (n + tiled::BN - 1) / tiled::BN;
+  bool same_k = true;
+  for (int i = 1; i < g.count; ++i) same_k = same_k && g.p[i].k == g.p[0].k;
   int best = 256;
   double best_t = 0;
-  for (int i = 0; i < 3; ++i) {
-    const int64_t blocks = nbn * ((m + bms[i] - 1) / bms[i]);
-    const double t = (double)((blocks + 255) / 256) * bms[i] / 256.0 / eff[i];
-    if (i == 0 || t < best_t - 1e-9) {
-      best = bms[i];
+  for (int j = 0; j < 3; ++j) {
+    int64_t blocks = 0;
+    double cost = 0, longest = 0;
+    for (int i = 0; i < g.count; ++i) {
+      const int64_t b = ((g.p[i].n + tiled::BN - 1) / tiled::BN) * ((g.p[i].m + bms[j] - 1) / bms[j]);
+      blocks += b;
+      cost += b * block_cost(bms[j], g.p[i].k);
+      longest = longest > block_cost(bms[j], g.p[i].k) ? longest : block_cost(bms[j], g.p[i].k);
+    }
+    const double t = same_k ? (double)((blocks + 255) / 256) * longest : (cost / 256 > longest ? cost / 256 : longest);
+    if (j == 0 || t < best_t - 1e-9) {
+      best = bms[j];
       best_t = t;
     }
   }
   return best;
 }
 
-hipError_t launch_gemm_tiled(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx, void* y,
-                             int64_t ldy, int out_f32, int block_m, hipStream_t s) {
-  const int bm = block_m > 0 ? block_m : tiled_block_m(pw->n, m);
+hipError_t launch_tiled_group(gemm_group& g, int out_f32, int block_m, hipStream_t s) {
+  // longest K first, so that the most expensive workgroups are dispatched first
+  for (int i = 1; i < g.count; ++i)
+    for (int j = i; j > 0 && g.p[j].k > g.p[j - 1].k; --j) {
+      const gemm_problem t = g.p[j];
+      g.p[j] = g.p[j - 1];
+      g.p[j - 1] = t;
+    }
+  const int bm = block_m > 0 ? block_m : tiled_block_m(g);
   switch (bm) {
     case 64:
-      return out_f32 ? launch_tiled_bm<true, 64>(pw, x, m, ldx, y, ldy, s) : launch_tiled_bm<false, 64>(pw, x, m, ldx, y, ldy, s);
+      return out_f32 ? launch_tiled_bm<true, 64>(g, s) : launch_tiled_bm<false, 64>(g, s);
     case 128:
-      return out_f32 ? launch_tiled_bm<true, 128>(pw, x, m, ldx, y, ldy, s) : launch_tiled_bm<false, 128>(pw, x, m, ldx, y, ldy, s);
+      return out_f32 ? launch_tiled_bm<true, 128>(g, s) : launch_tiled_bm<false, 128>(g, s);
     default:
-      return out_f32 ? launch_tiled_bm<true, 256>(pw, x, m, ldx, y, ldy, s) : launch_tiled_bm<false, 256>(pw, x, m, ldx, y, ldy, s);
+      return out_f32 ? launch_tiled_bm<true, 256>(g, s) : launch_tiled_bm<false, 256>(g, s);
   }
 }
 

@@ -48,12 +48,34 @@ hipError_t launch_decompress(const patch_weight* pw, uint16_t* w_out, int64_t ld
 hipError_t launch_mask_unpack(const uint8_t* bits, int64_t count, int order, uint8_t* out, hipStream_t s);
 
 // ---- GEMM kernels ----
-hipError_t launch_gemm_stream(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx,
-                              void* y, int64_t ldy, int out_f32, hipStream_t s);
-// block_m: X rows per workgroup (256, 128 or 64); 0 lets tiled_block_m choose.
-hipError_t launch_gemm_tiled(const patch_weight* pw, const uint16_t* x, int64_t m, int64_t ldx,
-                             void* y, int64_t ldy, int out_f32, int block_m, hipStream_t s);
-int tiled_block_m(int64_t n, int64_t m);
+// One product Y = X . Wm^T of a launch; a launch runs up to PATCH_MAX_GROUP of
+// them, passed by value as a kernel argument.
+#define PATCH_MAX_GROUP 16
+struct gemm_problem {
+  const int32_t* tile_desc;
+  const uint16_t* dense_vals;
+  const uint16_t* sparse_vals;
+  const uint8_t* sparse_meta;
+  const uint16_t* x;
+  void* y;
+  int64_t tiles_k, n, k, m, ldx, ldy;
+  int32_t tn, tk;
+  int32_t block0;  // first workgroup of this product in the launch
+  int32_t blocks;  // its workgroups (the launch may pad after them)
+};
+struct gemm_group {
+  int32_t count;
+  int32_t _pad;
+  gemm_problem p[PATCH_MAX_GROUP];
+};
+// The product of handle w with X [m][ldx] into Y [m][ldy] (block fields unset).
+gemm_problem make_problem(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y, int64_t ldy);
+// One launch of the streaming kernel (every m <= 16) / the tiled kernel over a
+// group.  block_m > 0 forces the tiled block height (256, 128, 64).
+hipError_t launch_stream_group(gemm_group& g, int out_f32, hipStream_t s);
+hipError_t launch_tiled_group(gemm_group& g, int out_f32, int block_m, hipStream_t s);
+// The tiled block height the launcher would pick for a group.
+int tiled_block_m(const gemm_group& g);
 hipError_t launch_fill_zero_y(void* y, int64_t m, int64_t n, int64_t ldy, int out_f32, hipStream_t s);
 
 // ---- device helpers ----

@@ -34,24 +34,25 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
-def test_info_struct_layout_matches_header(tmp_path):
-    """ctypes' patch_info must match what a C compiler makes of include/patch.h."""
+@pytest.mark.parametrize("cls,cname", [(api.PatchInfo, "patch_info"), (api.GemmItem, "patch_gemm_item")])
+def test_struct_layout_matches_header(tmp_path, cls, cname):
+    """ctypes' structs must match what a C compiler makes of include/patch.h."""
     import shutil
     import subprocess
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no C compiler")
-    fields = [f for f, _ in api.PatchInfo._fields_]
+    fields = [f for f, _ in cls._fields_]
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "patch.h"\nint main(void){\n'
-                   '  printf("%zu\\n", sizeof(patch_info));\n'
-                   + "".join(f'  printf("%zu\\n", offsetof(patch_info, {f}));\n' for f in fields)
+                   f'  printf("%zu\\n", sizeof({cname}));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof({cname}, {f}));\n' for f in fields)
                    + "  return 0;\n}\n")
     exe = tmp_path / "layout"
     subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
-    assert got[0] == ctypes.sizeof(api.PatchInfo)
-    assert got[1:] == [getattr(api.PatchInfo, f).offset for f in fields]
+    assert got[0] == ctypes.sizeof(cls)
+    assert got[1:] == [getattr(cls, f).offset for f in fields]
 
 
 def _pack(lib, w=1 << 20, n=128, k=128, ldw=128, bits=1 << 20, order=0, tn=64, tk=64):
@@ -103,3 +104,19 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setenv("PATCH_LIB", str(tmp_path / "missing.so"))
     with pytest.raises(api.PatchError):
         api.load()
+
+
+def test_grouped_argument_errors(lib):
+    """Rejected before any HIP call; the failing product is named."""
+    items = (api.GemmItem * 17)()
+    assert lib.patch_gemm_grouped(items, 0, 0, None) == 0            # empty group: no-op
+    assert lib.patch_gemm_grouped(None, 0, 0, None) == 0
+    assert lib.patch_gemm_grouped(None, 1, 0, None) == 1             # items NULL
+    assert lib.patch_gemm_grouped(items, 17, 0, None) == 1           # more than 16
+    assert b"0..16" in lib.patch_last_error()
+    assert lib.patch_gemm_grouped(items, -1, 0, None) == 1
+    assert lib.patch_gemm_grouped(items, 2, 9, None) == 1            # bad dtype
+    assert lib.patch_gemm_grouped(items, 2, 0, None) == 1            # NULL handles
+    assert lib.patch_last_error().startswith(b"product 0: weight handle is NULL")
+    assert lib.patch_gemm_grouped_kernel(items, 2, 0, 7, 0, None) == 1   # bad kernel
+    assert lib.patch_gemm_grouped_kernel(items, 2, 0, 1, 96, None) == 1  # bad block rows
