@@ -209,6 +209,35 @@ patch_status patch_get_info(const patch_weight* w, patch_info* info);
 patch_status patch_export(const patch_weight* w, uint8_t* tile_map, int32_t* tile_slot,
                           uint16_t* dense_vals, uint16_t* sparse_vals, uint8_t* sparse_meta);
 
+/*
+ * patch_import -- build a packed weight from the exported format: the inverse
+ * of patch_export, e.g. for a packed weight saved to a file and read back.
+ * The released artifact of the method is a mask over frozen base weights
+ * (model card "llama_3.2_1b-PATCH-45Sparse", description); this lets a model
+ * be packed once and loaded later without the dense W or the mask.
+ *
+ *   n, k, tile_n/k  as for patch_pack.
+ *   tile_map     host, (n/tile_n)*(k/tile_k) bytes, each PATCH_TILE_DENSE or
+ *                PATCH_TILE_SPARSE24; D and S are the counts of each.
+ *   dense_vals   host, D*tile_n*tile_k bf16 (may be NULL when D = 0).
+ *   sparse_vals  host, S*tile_n*tile_k/2 bf16.   sparse_meta  host,
+ *                S*tile_n*tile_k/8 bytes (both may be NULL when S = 0).
+ *                Layouts exactly as in the packed-format notes of patch_pack;
+ *                slots follow from the tile order.
+ *   stream, out, info  as for patch_pack.
+ *
+ * Errors, all found on the host before any device work: PATCH_E_SHAPE as for
+ * patch_pack; PATCH_E_INVALID_ARG for a tile_map byte other than 0 or 1, or a
+ * NULL pool that must hold data; PATCH_E_MASK for a 2:4 code that is not
+ * i0 | i1 << 2 with i0 < i1 (info->bad_tile / bad_row / bad_group locate it,
+ * as for patch_pack).  Ownership as for patch_pack: the host arrays may be
+ * freed on return.  Blocks the host until the copies are done.
+ * patch_export of the result returns the same arrays bit for bit.
+ */
+patch_status patch_import(int64_t n, int64_t k, int32_t tile_n, int32_t tile_k, const uint8_t* tile_map,
+                          const uint16_t* dense_vals, const uint16_t* sparse_vals, const uint8_t* sparse_meta,
+                          void* stream, patch_weight** out, patch_info* info);
+
 /* Free a handle and its device memory (NULL is a no-op).  The caller must make
  * sure no work using it is still in flight. */
 void patch_destroy(patch_weight* w);

@@ -4,10 +4,14 @@ The compute path is the C-ABI library ``libpatch.so`` (HIP kernels); this
 package is a thin ctypes binding over it.  Importing the package does not load
 the library; the first call does, and fails loudly if it is missing.
 """
-__all__ = ["pack", "mask_unpack", "PackedWeight", "PatchError", "lib_path"]
+__all__ = ["pack", "gemm_grouped", "import_packed", "mask_unpack", "PackedWeight", "PatchError", "lib_path",
+           "checkpoint"]
 
 
 def __getattr__(name):
+    if name == "checkpoint":
+        from . import checkpoint
+        return checkpoint
     if name in __all__:
         from . import api
         return getattr(api, name)

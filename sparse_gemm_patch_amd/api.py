@@ -24,7 +24,7 @@ DENSE, SPARSE24 = 0, 1
 
 # Exported entry points; kept in step with include/patch.h.
 SYMBOLS = ("patch_pack", "patch_gemm", "patch_gemm_kernel", "patch_gemm_grouped", "patch_gemm_grouped_kernel",
-           "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_destroy",
+           "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_import", "patch_destroy",
            "patch_last_error")
 MAX_GROUP = 16
 
@@ -81,12 +81,13 @@ def load() -> ctypes.CDLL:
     L.patch_mask_unpack.argtypes = [vp, i64, ctypes.c_int, vp, vp]
     L.patch_get_info.argtypes = [vp, ctypes.POINTER(PatchInfo)]
     L.patch_export.argtypes = [vp, vp, vp, vp, vp, vp]
+    L.patch_import.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(PatchInfo)]
     L.patch_destroy.argtypes = [vp]
     L.patch_destroy.restype = None
     L.patch_last_error.argtypes = []
     L.patch_last_error.restype = ctypes.c_char_p
     for name in ("patch_pack", "patch_gemm", "patch_gemm_kernel", "patch_gemm_grouped", "patch_gemm_grouped_kernel",
-                 "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export"):
+                 "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_import"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L
@@ -214,6 +215,36 @@ def gemm_grouped(products, outs=None, out_dtype: torch.dtype = torch.bfloat16, k
     if st:
         _raise(st)
     return outs
+
+
+PACKED_ARRAYS = ("tile_map", "dense_vals", "sparse_vals", "sparse_meta")
+
+
+def import_packed(arrays: dict, n: int, k: int, tile=(128, 128), device=None, stream=None) -> PackedWeight:
+    """Rebuild a packed weight from the arrays PackedWeight.export returns (tile_slot is implied
+    by tile_map and ignored).  The arrays are host numpy arrays; the weight lands on `device`."""
+    tn, tk = int(tile[0]), int(tile[1])
+    tm = np.ascontiguousarray(arrays["tile_map"], dtype=np.uint8).reshape(-1)
+    nd = int(np.count_nonzero(tm == DENSE))
+    ns = int(np.count_nonzero(tm == SPARSE24))
+    want = {"dense_vals": (np.uint16, nd * tn * tk), "sparse_vals": (np.uint16, ns * tn * tk // 2),
+            "sparse_meta": (np.uint8, ns * tn * tk // 8)}
+    host = {"tile_map": tm}
+    for key, (dt, size) in want.items():
+        a = np.ascontiguousarray(arrays[key])
+        if a.dtype != dt or a.size != size:
+            raise ValueError(f"{key}: expected {size} values of {np.dtype(dt).name}, got {a.size} of {a.dtype}")
+        host[key] = a.reshape(-1)
+    ptr = {key: (ctypes.c_void_p(a.ctypes.data) if a.size else None) for key, a in host.items()}
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    h = ctypes.c_void_p()
+    info = PatchInfo()
+    with torch.cuda.device(dev):
+        st = load().patch_import(int(n), int(k), tn, tk, ptr["tile_map"], ptr["dense_vals"], ptr["sparse_vals"],
+                                 ptr["sparse_meta"], _stream_handle(stream), ctypes.byref(h), ctypes.byref(info))
+    if st:
+        _raise(st, info.as_dict())
+    return PackedWeight(h, info.as_dict(), dev)
 
 
 def pack(w: torch.Tensor, bits: torch.Tensor, tile=(128, 128), bit_order: str = "big",

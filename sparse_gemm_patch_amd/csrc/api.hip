@@ -380,8 +380,20 @@ patch_status patch_get_info(const patch_weight* w, patch_info* info) {
   return ok();
 }
 
+static patch_status export_impl(const patch_weight* w, uint8_t* tile_map, int32_t* tile_slot, uint16_t* dense_vals,
+                                uint16_t* sparse_vals, uint8_t* sparse_meta);
+
 patch_status patch_export(const patch_weight* w, uint8_t* tile_map, int32_t* tile_slot, uint16_t* dense_vals,
                           uint16_t* sparse_vals, uint8_t* sparse_meta) {
+  try {
+    return export_impl(w, tile_map, tile_slot, dense_vals, sparse_vals, sparse_meta);
+  } catch (const std::bad_alloc&) {
+    return fail(PATCH_E_NOMEM, "host staging allocation failed");
+  }
+}
+
+static patch_status export_impl(const patch_weight* w, uint8_t* tile_map, int32_t* tile_slot, uint16_t* dense_vals,
+                                uint16_t* sparse_vals, uint8_t* sparse_meta) {
   if (!w) return fail(PATCH_E_INVALID_ARG, "weight handle is NULL");
   if (w->tiles == 0) return ok();
   hipError_t e = hipStreamSynchronize(w->last_stream);
@@ -438,6 +450,153 @@ patch_status patch_export(const patch_weight* w, uint8_t* tile_map, int32_t* til
               tmp[s * tn * tk / 8 + (u >> 2) * 512 + lane * 8 + (u & 3) * 2 + (bb & 1)];
         }
   }
+  return ok();
+}
+
+patch_status patch_import(int64_t n, int64_t k, int32_t tile_n, int32_t tile_k, const uint8_t* tile_map,
+                          const uint16_t* dense_vals, const uint16_t* sparse_vals, const uint8_t* sparse_meta,
+                          void* stream, patch_weight** out, patch_info* info) {
+  if (!out) return fail(PATCH_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  patch_status st = check_tile(n, k, tile_n, tile_k);
+  if (st != PATCH_OK) return st;
+  const int64_t tiles_n = n / tile_n, tiles_k = k / tile_k, tiles = tiles_n * tiles_k;
+  const int64_t tn = tile_n, tk = tile_k, bt = tn / 16;
+  if (tiles > 0 && !tile_map) return fail(PATCH_E_INVALID_ARG, "tile_map is NULL");
+  // Host-side validation of the exported format, before any device work.
+  int64_t nd = 0, ns = 0;
+  for (int64_t t = 0; t < tiles; ++t) {
+    if (tile_map[t] == PATCH_TILE_DENSE) ++nd;
+    else if (tile_map[t] == PATCH_TILE_SPARSE24) ++ns;
+    else return fail(PATCH_E_INVALID_ARG, "tile_map[%lld] = %d is neither dense (0) nor 2:4 (1)", (long long)t,
+                     (int)tile_map[t]);
+  }
+  if (nd > 0 && !dense_vals) return fail(PATCH_E_INVALID_ARG, "dense_vals is NULL but %lld tiles are dense", (long long)nd);
+  if (ns > 0 && (!sparse_vals || !sparse_meta))
+    return fail(PATCH_E_INVALID_ARG, "sparse_vals or sparse_meta is NULL but %lld tiles are 2:4", (long long)ns);
+  {
+    // every code must name two distinct kept positions i0 < i1
+    static const bool legal[16] = {false, false, false, false, true,  false, false, false,
+                                   true,  true,  false, false, true,  true,  true,  false};
+    int64_t slot = 0;
+    for (int64_t t = 0; t < tiles; ++t) {
+      if (tile_map[t] != PATCH_TILE_SPARSE24) continue;
+      const uint8_t* m = sparse_meta + slot * tn * tk / 8;
+      for (int64_t row = 0; row < tn; ++row)
+        for (int64_t g = 0; g < tk / 4; ++g) {
+          const int code = (m[row * (tk / 8) + g / 2] >> (4 * (g & 1))) & 15;
+          if (!legal[code]) {
+            if (info) {
+              memset(info, 0, sizeof(*info));
+              info->n = n;
+              info->k = k;
+              info->tile_n = tile_n;
+              info->tile_k = tile_k;
+              info->tiles_n = tiles_n;
+              info->tiles_k = tiles_k;
+              info->bad_tile = t;
+              info->bad_row = row;
+              info->bad_group = g;
+            }
+            return fail(PATCH_E_MASK, "2:4 code %d of tile %lld, row %lld, group %lld is not i0 | i1 << 2 with i0 < i1",
+                        code, (long long)t, (long long)row, (long long)g);
+          }
+        }
+      ++slot;
+    }
+  }
+  int dev = 0;
+  st = check_device(&dev);
+  if (st != PATCH_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  patch_weight* pw = new (std::nothrow) patch_weight();
+  if (!pw) return fail(PATCH_E_NOMEM, "host allocation failed");
+  pw->device = dev;
+  pw->n = n;
+  pw->k = k;
+  pw->tn = tile_n;
+  pw->tk = tile_k;
+  pw->tiles_n = tiles_n;
+  pw->tiles_k = tiles_k;
+  pw->tiles = tiles;
+  pw->n_dense = nd;
+  pw->n_sparse = ns;
+  pw->last_stream = s;
+  if (tiles == 0) {
+    if (info) fill_info(pw, info);
+    *out = pw;
+    return ok();
+  }
+  hipError_t e;
+#define PATCH_TRY(expr, what, status)                                    \
+  do {                                                                   \
+    e = (expr);                                                          \
+    if (e != hipSuccess) {                                               \
+      free_weight(pw);                                                   \
+      return status == PATCH_E_NOMEM                                     \
+                 ? fail(PATCH_E_NOMEM, "%s: %s", what, hipGetErrorString(e)) \
+                 : hip_fail(e, what);                                    \
+    }                                                                    \
+  } while (0)
+  const size_t dv = (size_t)nd * tn * tk * 2, sv = (size_t)ns * tn * tk, sm = (size_t)ns * tn * tk / 8;
+  PATCH_TRY(dev_alloc(reinterpret_cast<void**>(&pw->tile_map), (size_t)tiles), "device allocation", PATCH_E_NOMEM);
+  PATCH_TRY(dev_alloc(reinterpret_cast<void**>(&pw->tile_desc), (size_t)tiles * 4), "device allocation", PATCH_E_NOMEM);
+  PATCH_TRY(dev_alloc(reinterpret_cast<void**>(&pw->dense_vals), dv), "device allocation", PATCH_E_NOMEM);
+  PATCH_TRY(dev_alloc(reinterpret_cast<void**>(&pw->sparse_vals), sv), "device allocation", PATCH_E_NOMEM);
+  // +16 B: the streaming kernel reads 16 bytes at each lane's 8-byte code slot
+  PATCH_TRY(dev_alloc(reinterpret_cast<void**>(&pw->sparse_meta), sm + 16), "device allocation", PATCH_E_NOMEM);
+
+  // Descriptors (slot << 1 | type) and the pools in operand order: the inverse
+  // of the conversion in patch_export.
+  std::vector<int32_t> desc;
+  std::vector<uint16_t> dtmp, stmp;
+  std::vector<uint8_t> mtmp;
+  try {
+    desc.resize(tiles);
+    dtmp.resize(dv / 2);
+    stmp.resize(sv / 2);
+    mtmp.assign(sm + 16, 0);
+  } catch (const std::bad_alloc&) {
+    free_weight(pw);
+    return fail(PATCH_E_NOMEM, "host staging allocation failed");
+  }
+  {
+    int64_t cd = 0, cs = 0;
+    for (int64_t t = 0; t < tiles; ++t)
+      desc[t] = tile_map[t] == PATCH_TILE_DENSE ? (int32_t)((cd++) << 1) : (int32_t)(((cs++) << 1) | 1);
+  }
+  for (int64_t sl = 0; sl < nd; ++sl)
+    for (int64_t row = 0; row < tn; ++row)
+      for (int64_t col = 0; col < tk; ++col) {
+        const int64_t step = col / 64, cc = col % 64, q = cc / 16, within = cc % 16;
+        const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16, dw = within / 2;
+        const int64_t dst = sl * tn * tk + u * 1024 + (dw & 1) * 512 + lane * 8 + (dw >> 1) * 2 + (within & 1);
+        dtmp[dst] = dense_vals[(sl * tn + row) * tk + col];
+      }
+  for (int64_t sl = 0; sl < ns; ++sl)
+    for (int64_t row = 0; row < tn; ++row) {
+      for (int64_t c = 0; c < tk / 2; ++c) {
+        const int64_t step = c / 32, q = (c % 32) / 8, j = c % 8;
+        const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16;
+        stmp[sl * tn * tk / 2 + u * 512 + lane * 8 + j] = sparse_vals[(sl * tn + row) * (tk / 2) + c];
+      }
+      for (int64_t b = 0; b < tk / 8; ++b) {
+        const int64_t step = b / 8, bb = b % 8, q = bb / 2;
+        const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16;
+        mtmp[sl * tn * tk / 8 + (u >> 2) * 512 + lane * 8 + (u & 3) * 2 + (bb & 1)] =
+            sparse_meta[(sl * tn + row) * (tk / 8) + b];
+      }
+    }
+  PATCH_TRY(hipMemcpyAsync(pw->tile_map, tile_map, (size_t)tiles, hipMemcpyHostToDevice, s), "copy tile_map", 0);
+  PATCH_TRY(hipMemcpyAsync(pw->tile_desc, desc.data(), (size_t)tiles * 4, hipMemcpyHostToDevice, s), "copy descriptors", 0);
+  if (dv) PATCH_TRY(hipMemcpyAsync(pw->dense_vals, dtmp.data(), dv, hipMemcpyHostToDevice, s), "copy dense_vals", 0);
+  if (sv) PATCH_TRY(hipMemcpyAsync(pw->sparse_vals, stmp.data(), sv, hipMemcpyHostToDevice, s), "copy sparse_vals", 0);
+  if (sm) PATCH_TRY(hipMemcpyAsync(pw->sparse_meta, mtmp.data(), sm + 16, hipMemcpyHostToDevice, s), "copy sparse_meta", 0);
+  // the host staging buffers die on return
+  PATCH_TRY(hipStreamSynchronize(s), "hipStreamSynchronize", 0);
+#undef PATCH_TRY
+  if (info) fill_info(pw, info);
+  *out = pw;
   return ok();
 }
 

@@ -4,6 +4,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 from conftest import ROOT
@@ -120,3 +122,43 @@ def test_grouped_argument_errors(lib):
     assert lib.patch_last_error().startswith(b"product 0: weight handle is NULL")
     assert lib.patch_gemm_grouped_kernel(items, 2, 0, 7, 0, None) == 1   # bad kernel
     assert lib.patch_gemm_grouped_kernel(items, 2, 0, 1, 96, None) == 1  # bad block rows
+
+
+def _import(lib, n=128, k=128, tn=64, tk=64, tile_map=None, dense=True, sparse=True, meta=None):
+    tiles = (n // tn) * (k // tk) if n % tn == 0 and k % tk == 0 and tn in (64, 128) and tk in (64, 128) else 1
+    tm = np.full(tiles, 1, np.uint8) if tile_map is None else np.asarray(tile_map, np.uint8)
+    ns = int((tm == 1).sum())
+    nd = int((tm == 0).sum())
+    dv = np.zeros(max(nd * tn * tk, 1), np.uint16)
+    sv = np.zeros(max(ns * tn * tk // 2, 1), np.uint16)
+    sm = np.full(max(ns * tn * tk // 8, 1), 0x44, np.uint8) if meta is None else meta
+    h = ctypes.c_void_p(0xBEEF)
+    info = api.PatchInfo()
+    st = lib.patch_import(n, k, tn, tk, tm.ctypes.data, dv.ctypes.data if dense else None,
+                          sv.ctypes.data if sparse else None, sm.ctypes.data if sparse else None, None,
+                          ctypes.byref(h), ctypes.byref(info))
+    return st, h.value, info
+
+
+def test_import_argument_errors(lib):
+    """patch_import validates the exported format on the host before any HIP call."""
+    assert _import(lib, tn=32)[:2] == (2, None)                     # tile side
+    assert _import(lib, n=100)[:2] == (2, None)                     # ragged N
+    assert _import(lib, tile_map=[0, 1, 2, 1])[:2] == (1, None)     # not a tile type
+    assert b"tile_map[2]" in lib.patch_last_error()
+    assert _import(lib, tile_map=[0, 1, 1, 1], dense=False)[:2] == (1, None)   # dense pool missing
+    assert _import(lib, tile_map=[0, 1, 1, 1], sparse=False)[:2] == (1, None)  # 2:4 pools missing
+    st = lib.patch_import(128, 128, 64, 64, None, None, None, None, None, None, None)
+    assert st == 1                                                  # out == NULL
+
+
+@pytest.mark.parametrize("code", [0, 1, 2, 3, 5, 6, 7, 10, 11, 15])
+def test_import_rejects_illegal_codes(lib, code):
+    """Only the six codes i0 | i1 << 2 with i0 < i1 are legal; the first bad one is located."""
+    tm = np.array([0, 1, 0, 1], np.uint8)          # 64x64 tiles: slot 1 of the 2:4 pool is tile 3
+    meta = np.full(2 * 64 * 64 // 8, 0x44, np.uint8)
+    row, group = 17, 9                              # group 9 is the high nibble of byte 4 of the row
+    meta[64 * 64 // 8 + row * 8 + group // 2] = (code << 4) | 0x4
+    st, h, info = _import(lib, tile_map=tm, meta=meta)
+    assert (st, h) == (3, None)
+    assert (info.bad_tile, info.bad_row, info.bad_group) == (3, row, group)

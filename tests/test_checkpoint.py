@@ -1,0 +1,39 @@
+"""Mask-file reading (no GPU): the .npz forms the loader accepts and rejects."""
+import numpy as np
+import pytest
+
+from sparse_gemm_patch_amd import checkpoint as C
+from sparse_gemm_patch_amd import inputs as I
+
+
+def test_flat_and_row_packed_masks_read_the_same(tmp_path):
+    prob = I.make_problem("npz", 1, 128, 256, 64, 64, frac=0.5, cfg=70)
+    flat = prob.bits
+    rows = np.packbits(prob.mask.astype(np.uint8), axis=1)  # [out][in/8]
+    path = tmp_path / "mask.npz"
+    np.savez(path, **{"model.layers.0.mlp.up_proj.weight": flat, "model.layers.0.mlp.down_proj": rows})
+    m = C.read_mask_npz(str(path))
+    assert set(m) == {"model.layers.0.mlp.up_proj.weight", "model.layers.0.mlp.down_proj"}
+    assert np.array_equal(m["model.layers.0.mlp.up_proj.weight"], flat)
+    assert np.array_equal(m["model.layers.0.mlp.down_proj"], flat)  # same bytes when in % 8 == 0
+
+
+def test_unpacked_masks_are_rejected(tmp_path):
+    path = tmp_path / "mask.npz"
+    np.savez(path, a=np.ones((4, 8), bool))
+    with pytest.raises(ValueError):
+        C.read_mask_npz(str(path))
+
+
+def test_name_matching():
+    masks = {"a.weight": np.zeros(1, np.uint8), "b": np.zeros(1, np.uint8)}
+    assert C._match(masks, "a.weight") == "a.weight"
+    assert C._match(masks, "b.weight") == "b"
+    assert C._match(masks, "c.weight") is None
+
+
+def test_packed_file_needs_the_format_marker(tmp_path):
+    path = tmp_path / "x.npz"
+    np.savez(path, **{"q::shape": np.array([64, 64, 64, 64], np.int64)})
+    with pytest.raises(ValueError):
+        C.load_packed(str(path))
