@@ -7,3 +7,4 @@ from .patch_oracle import (DENSE, SPARSE24, LEGAL_CODES, TOL, MaskError, Packed,
                            bf16_to_f64, check_shape, classify, compress, decompress, gemm_brute,
                            gemm_ref, mask_of, masked_weight, measured_sparsity, rel_error,
                            tile_slots, unpack_bits, within_tolerance)
+from . import sample_oracle  # noqa: F401,E402
