@@ -9,10 +9,9 @@ __all__ = ["pack", "gemm_grouped", "import_packed", "mask_unpack", "PackedWeight
 
 
 def __getattr__(name):
+    import importlib
     if name == "checkpoint":
-        from . import checkpoint
-        return checkpoint
+        return importlib.import_module(".checkpoint", __name__)
     if name in __all__:
-        from . import api
-        return getattr(api, name)
+        return getattr(importlib.import_module(".api", __name__), name)
     raise AttributeError(name)
