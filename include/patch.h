@@ -210,6 +210,41 @@ patch_status patch_export(const patch_weight* w, uint8_t* tile_map, int32_t* til
                           uint16_t* dense_vals, uint16_t* sparse_vals, uint8_t* sparse_meta);
 
 /*
+ * patch_sample_mask -- the hard sample of a tile configuration: per tile the
+ * choice dense / 2:4, per group of four along K one of the six 2:4 patterns,
+ * written as a bit-packed keep mask that patch_pack accepts.
+ *
+ * PATCH learns a per-tile dense / 2:4 choice ("PATCH: Learnable Tile-level
+ * Hybrid Sparsity for LLMs", Abstract) from logits sampled with Gumbel noise
+ * under a scaling kappa and a temperature tau (model card
+ * "llama_3.2_1b-PATCH-45Sparse", "Training hyper-parameters": kappa 25 -> 350,
+ * tau 4 -> 0.05, logits initialised from N(0, 0.014)); the pattern inside a
+ * 2:4 group comes from logits over its candidate patterns (card
+ * "gemma_3_1b-MaskLLM-50Sparse", description).  Each choice takes the index
+ * of the largest score fl(fl(kappa * logit) + noise), computed in fp32 with
+ * one rounding per operation; the first maximum wins and a NaN score never
+ * wins (all-NaN or all -inf picks index 0).  tau divides every score of a
+ * choice by the same positive number, so it does not change a hard sample and
+ * is not an argument.
+ *
+ *   tile_logits   device f32 [tiles][2] (dense, 2:4), row-major tile order,
+ *                 tiles = (n/tile_n)*(k/tile_k).
+ *   tile_noise    device f32 [tiles][2], or NULL for no noise.
+ *   group_logits  device f32 [n][k/4][6]: per group, the patterns with kept
+ *                 positions (0,1) (0,2) (0,3) (1,2) (1,3) (2,3) in that order.
+ *   group_noise   device f32 [n][k/4][6], or NULL.
+ *   n, k, tile_n/k  as for patch_pack (PATCH_E_SHAPE otherwise).
+ *   kappa         scale of the logits.
+ *   mask_bits     device, n*k/8 bytes, written (bit order `order`; 1 = keep):
+ *                 dense tiles keep everything, 2:4 tiles the chosen pattern.
+ *
+ * All float pointers 4-byte aligned.  Never allocates, never blocks the host.
+ */
+patch_status patch_sample_mask(const float* tile_logits, const float* tile_noise, const float* group_logits,
+                               const float* group_noise, int64_t n, int64_t k, int32_t tile_n, int32_t tile_k,
+                               float kappa, patch_bit_order order, uint8_t* mask_bits, void* stream);
+
+/*
  * patch_import -- build a packed weight from the exported format: the inverse
  * of patch_export, e.g. for a packed weight saved to a file and read back.
  * The released artifact of the method is a mask over frozen base weights

@@ -4,7 +4,7 @@ The compute path is the C-ABI library ``libpatch.so`` (HIP kernels); this
 package is a thin ctypes binding over it.  Importing the package does not load
 the library; the first call does, and fails loudly if it is missing.
 """
-__all__ = ["pack", "gemm_grouped", "import_packed", "mask_unpack", "PackedWeight", "PatchError", "lib_path",
+__all__ = ["pack", "gemm_grouped", "import_packed", "sample_mask", "mask_unpack", "PackedWeight", "PatchError", "lib_path",
            "checkpoint"]
 
 

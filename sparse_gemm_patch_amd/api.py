@@ -24,8 +24,8 @@ DENSE, SPARSE24 = 0, 1
 
 # Exported entry points; kept in step with include/patch.h.
 SYMBOLS = ("patch_pack", "patch_gemm", "patch_gemm_kernel", "patch_gemm_grouped", "patch_gemm_grouped_kernel",
-           "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_import", "patch_destroy",
-           "patch_last_error")
+           "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_import",
+           "patch_sample_mask", "patch_destroy", "patch_last_error")
 MAX_GROUP = 16
 
 
@@ -82,12 +82,14 @@ def load() -> ctypes.CDLL:
     L.patch_get_info.argtypes = [vp, ctypes.POINTER(PatchInfo)]
     L.patch_export.argtypes = [vp, vp, vp, vp, vp, vp]
     L.patch_import.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(PatchInfo)]
+    L.patch_sample_mask.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, ctypes.c_float, ctypes.c_int, vp, vp]
     L.patch_destroy.argtypes = [vp]
     L.patch_destroy.restype = None
     L.patch_last_error.argtypes = []
     L.patch_last_error.restype = ctypes.c_char_p
     for name in ("patch_pack", "patch_gemm", "patch_gemm_kernel", "patch_gemm_grouped", "patch_gemm_grouped_kernel",
-                 "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_import"):
+                 "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_import",
+                 "patch_sample_mask"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L
@@ -267,6 +269,40 @@ def pack(w: torch.Tensor, bits: torch.Tensor, tile=(128, 128), bit_order: str = 
     if st:
         _raise(st, info.as_dict())
     return PackedWeight(h, info.as_dict(), w.device)
+
+
+def sample_mask(tile_logits: torch.Tensor, group_logits: torch.Tensor, n: int, k: int, tile=(128, 128),
+                kappa: float = 1.0, tile_noise: Optional[torch.Tensor] = None,
+                group_noise: Optional[torch.Tensor] = None, bit_order: str = "big",
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Hard sample of a tile configuration as bit-packed mask bits (uint8 [n*k/8] on the GPU).
+
+    tile_logits f32 [tiles][2] (dense, 2:4); group_logits f32 [n][k/4][6]; noise of the same
+    shapes or None."""
+    tn, tk = int(tile[0]), int(tile[1])
+    tiles = (n // tn) * (k // tk) if tn and tk else 0
+    shapes = {"tile_logits": (tile_logits, (tiles, 2)), "group_logits": (group_logits, (n, k // 4, 6)),
+              "tile_noise": (tile_noise, (tiles, 2)), "group_noise": (group_noise, (n, k // 4, 6))}
+    for name, (t, shape) in shapes.items():
+        if t is None:
+            if name.endswith("logits"):
+                raise ValueError(f"{name} is required")
+            continue
+        _check_cuda(t, name, torch.float32)
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous {shape}, got {tuple(t.shape)}")
+    if out is None:
+        out = torch.empty(n * k // 8, dtype=torch.uint8, device=tile_logits.device)
+    _check_cuda(out, "out", torch.uint8)
+    if out.numel() * 8 < n * k:
+        raise ValueError("out holds fewer than n*k bits")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    st = load().patch_sample_mask(ptr(tile_logits), ptr(tile_noise), ptr(group_logits), ptr(group_noise), int(n),
+                                  int(k), tn, tk, float(kappa), BIT_ORDER[bit_order], ptr(out),
+                                  _stream_handle(stream))
+    if st:
+        _raise(st)
+    return out
 
 
 def mask_unpack(bits: torch.Tensor, count: int, bit_order: str = "big", out: Optional[torch.Tensor] = None,

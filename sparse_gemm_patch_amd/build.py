@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpatch.so")
-SOURCES = ["api.hip", "pack.hip", "gemm.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemm.hip", "sample.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

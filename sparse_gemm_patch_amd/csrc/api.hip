@@ -453,6 +453,29 @@ static patch_status export_impl(const patch_weight* w, uint8_t* tile_map, int32_
   return ok();
 }
 
+patch_status patch_sample_mask(const float* tile_logits, const float* tile_noise, const float* group_logits,
+                               const float* group_noise, int64_t n, int64_t k, int32_t tile_n, int32_t tile_k,
+                               float kappa, patch_bit_order order, uint8_t* mask_bits, void* stream) {
+  if (order != PATCH_BITS_MSB_FIRST && order != PATCH_BITS_LSB_FIRST)
+    return fail(PATCH_E_INVALID_ARG, "bad bit order %d", (int)order);
+  patch_status st = check_tile(n, k, tile_n, tile_k);
+  if (st != PATCH_OK) return st;
+  if (n * k == 0) return ok();
+  if (!tile_logits || !group_logits || !mask_bits)
+    return fail(PATCH_E_INVALID_ARG, "tile_logits, group_logits and mask_bits must not be NULL");
+  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; };
+  if (misaligned(tile_logits) || misaligned(group_logits) || misaligned(tile_noise) || misaligned(group_noise))
+    return fail(PATCH_E_INVALID_ARG, "logits and noise must be 4-byte aligned");
+  int dev = 0;
+  st = check_device(&dev);
+  if (st != PATCH_OK) return st;
+  const hipError_t e = launch_sample_mask(tile_logits, tile_noise, group_logits, group_noise, n, k, tile_n, tile_k,
+                                          kappa, order == PATCH_BITS_LSB_FIRST, mask_bits,
+                                          reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sample launch");
+  return ok();
+}
+
 patch_status patch_import(int64_t n, int64_t k, int32_t tile_n, int32_t tile_k, const uint8_t* tile_map,
                           const uint16_t* dense_vals, const uint16_t* sparse_vals, const uint8_t* sparse_meta,
                           void* stream, patch_weight** out, patch_info* info) {

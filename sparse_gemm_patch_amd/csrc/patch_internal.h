@@ -46,6 +46,10 @@ hipError_t launch_compress(const uint16_t* w, int64_t ldw, const uint8_t* bits, 
                            hipStream_t s);
 hipError_t launch_decompress(const patch_weight* pw, uint16_t* w_out, int64_t ldw, hipStream_t s);
 hipError_t launch_mask_unpack(const uint8_t* bits, int64_t count, int order, uint8_t* out, hipStream_t s);
+// ---- hard tile-configuration sample (sample.hip) ----
+hipError_t launch_sample_mask(const float* tile_logits, const float* tile_noise, const float* group_logits,
+                              const float* group_noise, int64_t n, int64_t k, int tn, int tk, float kappa,
+                              int lsb_first, uint8_t* bits, hipStream_t s);
 
 // ---- GEMM kernels ----
 // One product Y = X . Wm^T of a launch; a launch runs up to PATCH_MAX_GROUP of

@@ -29,7 +29,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 SEED_BASE = 0x50415443  # "PATC"
-ROLE_W, ROLE_X, ROLE_TILES, ROLE_FRACTIONS = 0, 1, 2, 3
+ROLE_W, ROLE_X, ROLE_TILES, ROLE_FRACTIONS, ROLE_LOGITS = 0, 1, 2, 3, 4
 
 
 def rng_for(cfg: int, matrix: int, role: int) -> np.random.Generator:
@@ -178,3 +178,20 @@ def nonuniform_fractions(tile_counts: list[int], rng: np.random.Generator, lo: f
     for i in order[:max(rem, 0)]:
         s[i] += 1
     return f, [int(v) for v in s]
+
+
+def sample_inputs(n: int, k: int, tn: int, tk: int, rng: np.random.Generator, scale: float = 0.014,
+                  noise: bool = True):
+    """Seeded inputs of a hard tile-configuration sample: tile logits [T][2], group logits
+    [n][k/4][6] ~ N(0, scale) (the card's logit initialisation is N(0, 0.014)), and standard
+    Gumbel noise of the same shapes, -log(-log(u)) with u uniform in (0, 1), all float32."""
+    tiles = (n // tn) * (k // tk)
+    tl = rng.normal(0.0, scale, (tiles, 2)).astype(np.float32)
+    gl = rng.normal(0.0, scale, (n, k // 4, 6)).astype(np.float32)
+    if not noise:
+        return tl, gl, None, None
+    u = rng.random((tiles, 2))
+    tz = (-np.log(-np.log(u))).astype(np.float32)
+    u = rng.random((n, k // 4, 6))
+    gz = (-np.log(-np.log(u))).astype(np.float32)
+    return tl, gl, tz, gz

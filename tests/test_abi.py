@@ -162,3 +162,15 @@ def test_import_rejects_illegal_codes(lib, code):
     st, h, info = _import(lib, tile_map=tm, meta=meta)
     assert (st, h) == (3, None)
     assert (info.bad_tile, info.bad_row, info.bad_group) == (3, row, group)
+
+
+def test_sample_mask_argument_errors(lib):
+    f = ctypes.c_void_p(1 << 20)
+    assert lib.patch_sample_mask(f, None, f, None, 128, 128, 64, 64, 25.0, 7, f, None) == 1   # bad order
+    assert lib.patch_sample_mask(f, None, f, None, 128, 128, 64, 32, 25.0, 0, f, None) == 2   # tile side
+    assert lib.patch_sample_mask(f, None, f, None, 100, 128, 64, 64, 25.0, 0, f, None) == 2   # ragged N
+    assert lib.patch_sample_mask(None, None, f, None, 128, 128, 64, 64, 25.0, 0, f, None) == 1
+    assert lib.patch_sample_mask(f, None, f, None, 128, 128, 64, 64, 25.0, 0, None, None) == 1
+    g = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.patch_sample_mask(f, g, f, None, 128, 128, 64, 64, 25.0, 0, f, None) == 1      # misaligned
+    assert lib.patch_sample_mask(None, None, None, None, 0, 128, 64, 64, 25.0, 0, None, None) == 0  # empty
