@@ -101,6 +101,24 @@ def magnitude_mask(w_bits: np.ndarray, tile_sparse: np.ndarray, tn: int, tk: int
     return np.where(elem_sparse, top2, np.uint8(1)).astype(np.uint8)
 
 
+# Code i0 | i1 << 2 of a 2:4 group -> index of its pattern in the order
+# (0,1) (0,2) (0,3) (1,2) (1,3) (2,3).
+_PATTERN_OF_CODE = {4: 0, 8: 1, 12: 2, 9: 3, 13: 4, 14: 5}
+
+
+def magnitude_patterns(w_bits: np.ndarray) -> np.ndarray:
+    """int8[N][K/4]: per aligned group of four along K, the index of the 2:4 pattern that keeps
+    its two largest |w| (lower index first among equal magnitudes, as magnitude_mask)."""
+    n, k = w_bits.shape
+    mag = np.abs(bf16_bits_to_f32(w_bits)).reshape(n, k // 4, 4)
+    order = np.sort(np.argsort(-mag, axis=2, kind="stable")[:, :, :2], axis=2)
+    code = order[:, :, 0] | (order[:, :, 1] << 2)
+    lut = np.zeros(16, np.int8)
+    for c, p in _PATTERN_OF_CODE.items():
+        lut[c] = p
+    return lut[code]
+
+
 def pack_mask_bits(mask: np.ndarray, order: str = "big") -> np.ndarray:
     """Bit-pack a 0/1 mask, flattened row-major, with numpy.packbits ('big' = MSB first)."""
     return np.packbits(np.asarray(mask, dtype=np.uint8).reshape(-1), bitorder=order)
