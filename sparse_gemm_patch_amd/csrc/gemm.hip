@@ -234,17 +234,19 @@ template <int BM> constexpr int x_bytes() { return BM * 128; }
 template <int BM> constexpr int stage_bytes() { return x_bytes<BM>() + 4 * G_BYTES; }
 }  // namespace tiled
 
-// global -> LDS copy of 16 (or 4) bytes per lane; lane i writes LDS bytes
-// lds_addr + 16 i (4 i).  lds_addr must be wave-uniform.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+// global -> LDS copy of 16 (or 4) bytes per lane from base + off (base
+// wave-uniform, off a 32-bit per-lane byte offset); lane i writes LDS bytes
+// lds_addr + 16 i (4 i).  lds_addr must be wave-uniform.  A scalar base keeps
+// one VGPR per copy stream instead of a 64-bit address.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
   uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(lds_addr), "v"(src) : "memory");
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(off), "s"(base) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds_addr) {
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds_addr) {
   uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(lds_addr), "v"(src) : "memory");
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(off), "s"(base) : "memory");
 }
 // Wait for this wave's copies and LDS reads, then synchronise the workgroup.
 __device__ __forceinline__ void step_barrier() {
@@ -312,35 +314,40 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
   const int ns = tn == 128 ? 7 : 6;   // log2(TN)
   const int bt = tn >> 4;             // 16-row blocks per tile
 
-  // ---- copy roles: X rows BM/8 wave + 8 j + (lane >> 3), logical chunk (lane & 7) ^ (row & 7)
-  // (rows past M clamp to M - 1: they only feed Y rows that are never stored),
-  // and half (wave & 1) of W group wave >> 1 (rows n0 + 64 (wave >> 1) .. +63).
-  const uint16_t* xp[XB];
+  // ---- copy roles: waves 4-7 (the second wave on each SIMD) copy the whole
+  // step; waves 0-3 only compute, so they start their smfmacs right after the
+  // barrier while the copies queue up behind the vector-memory path.  Copy
+  // wave c = wave - 4 takes X rows BM/4 c .. +BM/4-1 (8 rows per 1 KiB copy,
+  // logical chunk (lane & 7) ^ (row & 7); rows past M clamp to M - 1, they only
+  // feed Y rows that are never stored) and W group c (rows n0 + 64 c .. +63).
+  const bool copier = wave >= 4;
+  const int cw = wave & 3;
+  constexpr int XC = BM / 32;  // X copies per copy wave
+  const uint8_t* xblk = reinterpret_cast<const uint8_t*>(x + m0 * ldx);
+  uint32_t xoff[XC];
 #pragma unroll
-  for (int j = 0; j < XB; ++j) {
-    const int row = BM / 8 * wave + 8 * j + (lane >> 3);
+  for (int j = 0; j < XC; ++j) {
+    const int row = BM / 4 * cw + 8 * j + (lane >> 3);
     int64_t gm = m0 + row;
     if (gm > m - 1) gm = m - 1;
-    xp[j] = x + gm * ldx + 8 * ((lane & 7) ^ xswz(row));
+    xoff[j] = (uint32_t)(((gm - m0) * ldx + 8 * ((lane & 7) ^ xswz(row))) * 2);
   }
-  const int cg = wave >> 1, chalf = wave & 1;  // copied group and half of its copies
-  const int64_t gn0 = n0 + 64 * cg;
+  const int64_t gn0 = n0 + 64 * cw;
   const bool g_ok = gn0 < n;
   const int64_t g_desc = (gn0 >> ns) * tiles_k;
   const int g_blk = (int)((gn0 & (tn - 1)) >> 4);
-  const uint8_t* dsrc = reinterpret_cast<const uint8_t*>(dense_vals) + lane * 16;
-  const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(sparse_vals) + lane * 16;
-  const uint8_t* msrc = sparse_meta + lane * 4;
+  const uint8_t* dsrc = reinterpret_cast<const uint8_t*>(dense_vals);
+  const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(sparse_vals);
+  const uint32_t loff16 = lane * 16, loff4 = lane * 4;
 
-  // A group's 8 KiB: dense = 8 blocks of 1 KiB (half h copies blocks
-  // 4 h .. 4 h + 3); 2:4 = 4 value blocks (half 0) and 512 B of codes (half 1,
-  // two 256 B copies).  The barrier waits for all of a wave's copies, so their
-  // number may differ between waves.
+  // A group's 8 KiB: dense = 8 blocks of 1 KiB; 2:4 = 4 value blocks and 512 B
+  // of codes at +4 KiB (two 256 B copies).
   auto issue = [&](int step, int stage) {
+    if (!copier) return;
     const uint32_t st = lds_base + stage * STAGE_BYTES;
 #pragma unroll
-    for (int j = 0; j < XB; ++j) dma16(xp[j] + step * 64, st + (BM / 8 * wave + 8 * j) * 128);
-    const uint32_t g = st + X_BYTES + cg * G_BYTES;
+    for (int j = 0; j < XC; ++j) dma16(xblk + step * 128, xoff[j], st + (BM / 4 * cw + 8 * j) * 128);
+    const uint32_t g = st + X_BYTES + cw * G_BYTES;
     if (!g_ok) return;  // group past N
     const int32_t d = tile_desc[g_desc + (step >> ks)];
     const int64_t slot = d >> 1;
@@ -348,15 +355,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
     if ((d & 1) == PATCH_TILE_DENSE) {
       const uint8_t* src = dsrc + (slot * tn * tk + u0 * 1024) * 2;
 #pragma unroll
-      for (int j = 4 * chalf; j < 4 * chalf + 4; ++j) dma16(src + 1024 * j, g + 1024 * j);
-    } else if (chalf == 0) {
+      for (int j = 0; j < 8; ++j) dma16(src + 1024 * j, loff16, g + 1024 * j);
+    } else {
       const uint8_t* src = ssrc + slot * tn * tk + u0 * 1024;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(src + 1024 * j, g + 1024 * j);
-    } else {
-      const uint8_t* mp = msrc + slot * tn * (tk >> 3) + (u0 >> 2) * 512;
-      dma4(mp, g + 4096);
-      dma4(mp + 256, g + 4096 + 256);
+      for (int j = 0; j < 4; ++j) dma16(src + 1024 * j, loff16, g + 1024 * j);
+      const uint8_t* mp = sparse_meta + slot * tn * (tk >> 3) + (u0 >> 2) * 512;
+      dma4(mp, loff4, g + 4096);
+      dma4(mp + 256, loff4, g + 4096 + 256);
     }
   };
 
