@@ -119,3 +119,23 @@ def test_13b_mixed_tiles(P, shape, tile, frac):
     n, k = shape
     prob = I.make_problem("13b", 2048, n, k, tile[0], tile[1], frac=frac, cfg=5, matrix=n % 7)
     check_problem(P, prob, seed=500 + n, repeat=False)
+
+
+@pytest.mark.parametrize("stage", [["q", "k", "v"], ["gate", "up"]], ids=["qkv", "gate_up"])
+def test_llama1b_grouped_stage_bench_inputs(P, stage):
+    """The benchmark's grouped stages at full size: every product equals its solo launch bit
+    for bit, and sampled rows match the oracle."""
+    names = [k for k, _ in LLAMA1B]
+    probs = [I.make_problem(lbl, 4096, *I.LLAMA32_1B[lbl], 128, 128, frac=0.9, cfg=1, matrix=names.index(lbl))
+             for lbl in stage]
+    pws = [P.pack(dev_u16(p.w), torch.from_numpy(p.bits).cuda(), tile=(128, 128)) for p in probs]
+    xs = [dev_u16(p.x) for p in probs]
+    ys = P.gemm_grouped(list(zip(pws, xs)))
+    solo = [pw.gemm(x) for pw, x in zip(pws, xs)]
+    torch.cuda.synchronize()
+    for i, (p, y, s) in enumerate(zip(probs, ys, solo)):
+        assert torch.equal(y, s), stage[i]
+        rows = sample_rows(p.m, 600 + i)
+        got = y[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+        ref = O.gemm_ref(p.x[rows], O.masked_weight(p.w, p.mask))
+        assert O.rel_error(got, ref) <= TOL, stage[i]
