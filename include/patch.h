@@ -54,6 +54,9 @@ typedef enum { PATCH_BITS_MSB_FIRST = 0, PATCH_BITS_LSB_FIRST = 1 } patch_bit_or
 
 typedef enum { PATCH_OUT_BF16 = 0, PATCH_OUT_F32 = 1 } patch_out_dtype;
 
+/* Largest X leading dimension (elements) patch_gemm accepts: 2^22. */
+#define PATCH_MAX_LDX 4194304LL
+
 typedef enum { PATCH_TILE_DENSE = 0, PATCH_TILE_SPARSE24 = 1 } patch_tile_type;
 
 /* Kernel selection for patch_gemm_kernel.  AUTO picks STREAM for M <= 16 and
@@ -123,7 +126,7 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
  * Wm is W with the pruned weights zeroed (card "How to use").  Dense tiles run
  * on bf16 MFMA, 2:4 tiles on smfmac, so only kept weights are multiplied.
  *
- *   x      device, bf16 [m][ldx], ldx >= k, ldx % 8 == 0.
+ *   x      device, bf16 [m][ldx], k <= ldx <= PATCH_MAX_LDX, ldx % 8 == 0.
  *   m      >= 0 rows of X (0 is a no-op).
  *   y      device, [m][ldy] of bf16 (round to nearest even) or fp32,
  *          ldy >= n, ldy % 8 == 0.  Written, never read.  Must not alias x.

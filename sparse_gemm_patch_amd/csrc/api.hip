@@ -254,6 +254,9 @@ static patch_status check_product(const patch_weight* w, const uint16_t* x, int6
     if (!x) return fail(PATCH_E_INVALID_ARG, "x is NULL");
     if (!aligned16(x)) return fail(PATCH_E_INVALID_ARG, "x must be 16-byte aligned");
     if (ldx < w->k || ldx % 8) return fail(PATCH_E_INVALID_ARG, "ldx %lld must be >= k and a multiple of 8", (long long)ldx);
+    // the tiled kernel addresses a block's X rows with 32-bit byte offsets
+    if (ldx > PATCH_MAX_LDX)
+      return fail(PATCH_E_INVALID_ARG, "ldx %lld exceeds %lld", (long long)ldx, (long long)PATCH_MAX_LDX);
   }
   return ok();
 }

@@ -174,3 +174,8 @@ def test_sample_mask_argument_errors(lib):
     g = ctypes.c_void_p((1 << 20) + 2)
     assert lib.patch_sample_mask(f, g, f, None, 128, 128, 64, 64, 25.0, 0, f, None) == 1      # misaligned
     assert lib.patch_sample_mask(None, None, None, None, 0, 128, 64, 64, 25.0, 0, None, None) == 0  # empty
+
+
+def test_header_max_ldx():
+    text = open(HEADER).read()
+    assert re.search(r"#define PATCH_MAX_LDX 4194304LL", text)

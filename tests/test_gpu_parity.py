@@ -287,3 +287,15 @@ def test_gemm_m_zero_is_noop(P):
     pw = pack_problem(P, prob)
     x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
     assert tuple(pw.gemm(x).shape) == (0, 128)
+
+
+def test_ldx_limit(P):
+    """X rows farther apart than PATCH_MAX_LDX elements are refused, not mis-addressed."""
+    prob = I.make_problem("ldxmax", 2, 128, 128, 64, 64, frac=0.5, cfg=45)
+    pw = pack_problem(P, prob)
+    lib = P.load()
+    y = torch.empty((2, 128), dtype=torch.bfloat16, device="cuda")
+    x = dev_u16(prob.x)
+    st = lib.patch_gemm(pw._h, x.data_ptr(), 1, (1 << 22) + 8, y.data_ptr(), 128, 0, None)
+    assert P.STATUS[st] == "PATCH_E_INVALID_ARG"
+    assert b"exceeds" in lib.patch_last_error()
