@@ -34,7 +34,7 @@ def test_nonuniform_layer_hits_the_global_target():
 
 
 def test_rotation_covers_twice_the_infinity_cache():
-    for wb in (1 << 20, 43_000_000, 130_000_000, 600_000_000):
+    for wb in (16 << 20, 43_000_000, 130_000_000, 600_000_000):
         r = bench.rotation(wb)
         assert r * wb >= 2 * bench.MALL_BYTES and (r - 1) * wb < 2 * bench.MALL_BYTES
     assert 1 <= bench.rotation(0) <= 64
