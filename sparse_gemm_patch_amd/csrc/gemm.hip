@@ -252,6 +252,7 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t ld
 __device__ __forceinline__ void step_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ bf16x8 lds8(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ int xswz(int r) { return r & 7; }
 
@@ -460,6 +461,205 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
   }
 }
 
+// ------------------------------------------------------------------------
+// Warp-specialised kernel for 128 X rows per block: 12 waves.  Waves 0-7
+// compute exactly as in k_gemm_tiled with BM = 128 (2 x 4 grid, 128 W rows x 32
+// X rows each, two per SIMD); waves 8-11 (one per SIMD) only copy, two steps
+// ahead through three 48 KiB LDS stages.  A wave that issues copies stalls
+// while the per-CU fill path drains; here no computing wave ever does, and
+// the third stage hides the copies' latency.
+// ------------------------------------------------------------------------
+namespace wsk {
+constexpr int BM = 128, STAGES = 3, WAVES = 12;
+constexpr int X_BYTES = BM * 128;                              // 16 KiB
+constexpr int STAGE_BYTES = X_BYTES + 4 * tiled::G_BYTES;      // 48 KiB
+constexpr int XC = 4;                                          // X copies per copy wave (32 rows)
+}  // namespace wsk
+
+// Wait until at most n (XC, XC + 6 or XC + 8) of this wave's copies are
+// outstanding, and for its LDS reads.
+__device__ __forceinline__ void wait_copies_but(int n) {
+  switch (n) {
+    case 12: asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
+  }
+}
+
+template <bool F32>
+__global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
+  using namespace wsk;
+  using tiled::G_BYTES;
+  int local;
+  const int pi = find_problem(g, blockIdx.x, local);
+  if (pi < 0) return;
+  const gemm_problem& P = g.p[pi];
+  const const_desc_ptr tile_desc = (const_desc_ptr)P.tile_desc;
+  const int tn = P.tn, tk = P.tk;
+  const int64_t tiles_k = P.tiles_k, n = P.n, k = P.k, m = P.m;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t n0, m0;
+  block_origin<BM>(n, m, local, n0, m0);
+  const int nsteps = (int)(k / 64);
+  const int ks = tk == 128;
+  const int ns = tn == 128 ? 7 : 6;
+  const int bt = tn >> 4;
+
+  if (wave >= 8) {
+    // ---- copy waves: X rows 32 c .. 32 c + 31 and W group c (rows n0 + 64 c ..)
+    const int cw = wave - 8;
+    const int64_t ldx = P.ldx;
+    const uint8_t* xblk = reinterpret_cast<const uint8_t*>(P.x + m0 * ldx);
+    uint32_t xoff[XC];
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+      const int row = 32 * cw + 8 * j + (lane >> 3);
+      int64_t gm = m0 + row;
+      if (gm > m - 1) gm = m - 1;  // rows past M only feed Y rows that are never stored
+      xoff[j] = (uint32_t)(((gm - m0) * ldx + 8 * ((lane & 7) ^ xswz(row))) * 2);
+    }
+    const int64_t gn0 = n0 + 64 * cw;
+    const bool g_ok = gn0 < n;
+    const int64_t g_desc = (gn0 >> ns) * tiles_k;
+    const int g_blk = (int)((gn0 & (tn - 1)) >> 4);
+    const uint8_t* dsrc = reinterpret_cast<const uint8_t*>(P.dense_vals);
+    const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(P.sparse_vals);
+    const uint8_t* msrc = P.sparse_meta;
+    const uint32_t loff16 = lane * 16, loff4 = lane * 4;
+    auto issue = [&](int step, int stage) -> int {
+      const uint32_t st = lds_base + stage * STAGE_BYTES;
+#pragma unroll
+      for (int j = 0; j < XC; ++j) dma16(xblk + step * 128, xoff[j], st + (32 * cw + 8 * j) * 128);
+      const uint32_t gl = st + X_BYTES + cw * G_BYTES;
+      if (!g_ok) return XC;
+      const int32_t d = tile_desc[g_desc + (step >> ks)];
+      const int64_t slot = d >> 1;
+      const int64_t u0 = (step & ks) * bt + g_blk;
+      if ((d & 1) == PATCH_TILE_DENSE) {
+        const uint8_t* src = dsrc + (slot * tn * tk + u0 * 1024) * 2;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma16(src + 1024 * j, loff16, gl + 1024 * j);
+        return XC + 8;
+      }
+      const uint8_t* src = ssrc + slot * tn * tk + u0 * 1024;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(src + 1024 * j, loff16, gl + 1024 * j);
+      const uint8_t* mp = msrc + slot * tn * (tk >> 3) + (u0 >> 2) * 512;
+      dma4(mp, loff4, gl + 4096);
+      dma4(mp + 256, loff4, gl + 4096 + 256);
+      return XC + 6;
+    };
+    // Two steps ahead.  Before the barrier of step i this wave waits only for
+    // its copies of step i (those of step i + 1 were issued after them; vmcnt
+    // counts in issue order).  After it, every wave is done with step i - 1,
+    // whose stage takes step i + 2.
+    int pending = 0;
+    if (nsteps > 0) issue(0, 0);
+    if (nsteps > 1) pending = issue(1, 1);
+    int stage = 0;
+    for (int i = 0; i < nsteps; ++i) {
+      wait_copies_but(i + 1 < nsteps ? pending : 0);
+      barrier();
+      if (i + 2 < nsteps) pending = issue(i + 2, stage == 0 ? 2 : stage - 1);
+      stage = stage == 2 ? 0 : stage + 1;
+    }
+    return;
+  }
+
+  // ---- compute waves: W rows 128 wn .. +127, X rows 32 wm .. +31
+  const int wn = wave >> 2, wm = wave & 3;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int64_t wrow0 = n0 + 128 * wn;
+  const bool hok0 = wrow0 < n, hok1 = wrow0 + 64 < n;
+  const int64_t hdesc0 = (wrow0 >> ns) * tiles_k, hdesc1 = ((wrow0 + 64) >> ns) * tiles_k;
+  f32x4 acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int step, int stage) {
+    const uint8_t* cur = lds + stage * STAGE_BYTES;
+    const int d0 = hok0 ? ((tile_desc[hdesc0 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
+    const int d1 = hok1 ? ((tile_desc[hdesc1 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
+    bf16x16 b[2];
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm) {
+      const int r = 32 * wm + 16 * bm + r16;
+      b[bm] = cat16(lds8(cur + r * 128 + ((q ^ xswz(r)) << 4)), lds8(cur + r * 128 + (((4 + q) ^ xswz(r)) << 4)));
+    }
+    bf16x8 a0[8], a1[8];
+    int ix[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int dh = h ? d1 : d0;
+      const uint8_t* gp = cur + X_BYTES + (2 * wn + h) * G_BYTES;
+      if (dh > 0) {
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+          a0[4 * h + b4] = lds8(gp + 2048 * b4 + lane * 16);
+          a1[4 * h + b4] = lds8(gp + 2048 * b4 + 1024 + lane * 16);
+          ix[4 * h + b4] = 0x44444444;
+        }
+      } else if (dh == 0) {
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) a0[4 * h + b4] = lds8(gp + 1024 * b4 + lane * 16);
+        const uint2 c = *reinterpret_cast<const uint2*>(gp + 4096 + 8 * lane);
+        ix[4 * h + 0] = ix[4 * h + 1] = (int)c.x;
+        ix[4 * h + 2] = ix[4 * h + 3] = (int)c.y;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int dh = h ? d1 : d0;
+      if (dh < 0) continue;
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const int bn = 4 * h + b4;
+          acc[bn][bm] = b4 & 1 ? __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b[bm], acc[bn][bm], ix[bn], 0, 1)
+                               : __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b[bm], acc[bn][bm], ix[bn], 0, 0);
+        }
+      if (dh > 0) {
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const int bn = 4 * h + b4;
+            acc[bn][bm] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a1[bn], b[bm], acc[bn][bm], 0xEEEE, 0, 0);
+          }
+      }
+    }
+  };
+  int stage = 0;
+  for (int i = 0; i < nsteps; ++i) {
+    wait_copies_but(0);  // this wave's LDS reads of the previous step are done
+    barrier();           // step i is in `stage`
+    compute(i, stage);
+    stage = stage == 2 ? 0 : stage + 1;
+  }
+  void* __restrict__ y = P.y;
+  const int64_t ldy = P.ldy;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h == 0 ? !hok0 : !hok1) continue;
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm) {
+      const int64_t mm = m0 + 32 * wm + 16 * bm + r16;
+      if (mm >= m) continue;
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const int bn = 4 * h + b4;
+        const f32x4 v = acc[bn][bm];
+        store4<F32>(y, ldy, mm, wrow0 + 16 * bn + 4 * q, v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
 template <bool F32>
 __global__ void k_fill_zero_y(void* y, int64_t m, int64_t n, int64_t ldy) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -528,10 +728,32 @@ hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool F32>
+hipError_t launch_ws(gemm_group& g, hipStream_t s) {
+  constexpr int lds_bytes = wsk::STAGES * wsk::STAGE_BYTES;  // 144 KiB
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<F32>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int64_t total = 0;
+  for (int i = 0; i < g.count; ++i) {
+    g.p[i].block0 = (int32_t)total;
+    g.p[i].blocks = (int32_t)(((g.p[i].n + tiled::BN - 1) / tiled::BN) * ((g.p[i].m + wsk::BM - 1) / wsk::BM));
+    total += (g.p[i].blocks + 7) / 8 * 8;
+  }
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm_ws<F32>), dim3((unsigned)total), dim3(64 * wsk::WAVES), lds_bytes, s, g);
+  return hipGetLastError();
+}
+
 // Relative cost of one workgroup: block height over its measured efficiency
 // (smaller blocks move more LDS bytes per flop), times the K steps.
 double block_cost(int bm, int64_t k) {
-  const double eff = bm == 256 ? 1.0 : bm == 128 ? 0.69 : 0.42;  // measured on the LLaMA-3.2-1B projections
+  // measured in whole rounds on the 8192x2048 and 4096x4096 products at M = 4096
+  const double eff = bm == 256 ? 1.0 : bm == 128 ? 0.93 : 0.68;
   return bm / 256.0 / eff * (double)(k / 64);
 }
 }  // namespace
@@ -576,7 +798,7 @@ hipError_t launch_tiled_group(gemm_group& g, int out_f32, int block_m, hipStream
     case 64:
       return out_f32 ? launch_tiled_bm<true, 64>(g, s) : launch_tiled_bm<false, 64>(g, s);
     case 128:
-      return out_f32 ? launch_tiled_bm<true, 128>(g, s) : launch_tiled_bm<false, 128>(g, s);
+      return out_f32 ? launch_ws<true>(g, s) : launch_ws<false>(g, s);
     default:
       return out_f32 ? launch_tiled_bm<true, 256>(g, s) : launch_tiled_bm<false, 256>(g, s);
   }
