@@ -470,27 +470,31 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
 // the third stage hides the copies' latency.
 // ------------------------------------------------------------------------
 namespace wsk {
-constexpr int BM = 128, STAGES = 3, WAVES = 12;
-constexpr int X_BYTES = BM * 128;                              // 16 KiB
-constexpr int STAGE_BYTES = X_BYTES + 4 * tiled::G_BYTES;      // 48 KiB
-constexpr int XC = 4;                                          // X copies per copy wave (32 rows)
+constexpr int STAGES = 3, WAVES = 12;
+template <int BM> constexpr int stage_bytes() { return BM * 128 + 4 * tiled::G_BYTES; }  // 48 KiB at 128 rows
 }  // namespace wsk
 
-// Wait until at most n (XC, XC + 6 or XC + 8) of this wave's copies are
-// outstanding, and for its LDS reads.
+// Wait until at most n (XC, XC + 6 or XC + 8 with XC = 2 or 4) of this wave's
+// copies are outstanding, and for its LDS reads.
 __device__ __forceinline__ void wait_copies_but(int n) {
   switch (n) {
     case 12: asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory"); break;
     case 10: asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory"); break;
     case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory"); break;
     default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
   }
 }
 
-template <bool F32>
+template <bool F32, int BM>
 __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
   using namespace wsk;
   using tiled::G_BYTES;
+  constexpr int X_BYTES = BM * 128, STAGE_BYTES = stage_bytes<BM>();
+  constexpr int RW = BM / 4;   // X rows per copy wave and per compute wave
+  constexpr int XC = RW / 8;   // X copies per copy wave
+  constexpr int XB = RW / 16;  // X blocks of 16 rows per compute wave
   int local;
   const int pi = find_problem(g, blockIdx.x, local);
   if (pi < 0) return;
@@ -518,7 +522,7 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
     uint32_t xoff[XC];
 #pragma unroll
     for (int j = 0; j < XC; ++j) {
-      const int row = 32 * cw + 8 * j + (lane >> 3);
+      const int row = RW * cw + 8 * j + (lane >> 3);
       int64_t gm = m0 + row;
       if (gm > m - 1) gm = m - 1;  // rows past M only feed Y rows that are never stored
       xoff[j] = (uint32_t)(((gm - m0) * ldx + 8 * ((lane & 7) ^ xswz(row))) * 2);
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
     auto issue = [&](int step, int stage) -> int {
       const uint32_t st = lds_base + stage * STAGE_BYTES;
 #pragma unroll
-      for (int j = 0; j < XC; ++j) dma16(xblk + step * 128, xoff[j], st + (32 * cw + 8 * j) * 128);
+      for (int j = 0; j < XC; ++j) dma16(xblk + step * 128, xoff[j], st + (RW * cw + 8 * j) * 128);
       const uint32_t gl = st + X_BYTES + cw * G_BYTES;
       if (!g_ok) return XC;
       const int32_t d = tile_desc[g_desc + (step >> ks)];
@@ -577,17 +581,19 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
   const int64_t wrow0 = n0 + 128 * wn;
   const bool hok0 = wrow0 < n, hok1 = wrow0 + 64 < n;
   const int64_t hdesc0 = (wrow0 >> ns) * tiles_k, hdesc1 = ((wrow0 + 64) >> ns) * tiles_k;
-  f32x4 acc[8][2];
+  f32x4 acc[8][XB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < XB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int step, int stage) {
     const uint8_t* cur = lds + stage * STAGE_BYTES;
     const int d0 = hok0 ? ((tile_desc[hdesc0 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
     const int d1 = hok1 ? ((tile_desc[hdesc1 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
-    bf16x16 b[2];
+    bf16x16 b[XB];
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm) {
-      const int r = 32 * wm + 16 * bm + r16;
+    for (int bm = 0; bm < XB; ++bm) {
+      const int r = RW * wm + 16 * bm + r16;
       b[bm] = cat16(lds8(cur + r * 128 + ((q ^ xswz(r)) << 4)), lds8(cur + r * 128 + (((4 + q) ^ xswz(r)) << 4)));
     }
     bf16x8 a0[8], a1[8];
@@ -616,7 +622,7 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
       const int dh = h ? d1 : d0;
       if (dh < 0) continue;
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
+      for (int bm = 0; bm < XB; ++bm)
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) {
           const int bn = 4 * h + b4;
@@ -625,7 +631,7 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
         }
       if (dh > 0) {
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm)
+        for (int bm = 0; bm < XB; ++bm)
 #pragma unroll
           for (int b4 = 0; b4 < 4; ++b4) {
             const int bn = 4 * h + b4;
@@ -647,8 +653,8 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
   for (int h = 0; h < 2; ++h) {
     if (h == 0 ? !hok0 : !hok1) continue;
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm) {
-      const int64_t mm = m0 + 32 * wm + 16 * bm + r16;
+    for (int bm = 0; bm < XB; ++bm) {
+      const int64_t mm = m0 + RW * wm + 16 * bm + r16;
       if (mm >= m) continue;
 #pragma unroll
       for (int b4 = 0; b4 < 4; ++b4) {
@@ -728,12 +734,12 @@ hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool F32>
+template <bool F32, int BM>
 hipError_t launch_ws(gemm_group& g, hipStream_t s) {
-  constexpr int lds_bytes = wsk::STAGES * wsk::STAGE_BYTES;  // 144 KiB
+  constexpr int lds_bytes = wsk::STAGES * wsk::stage_bytes<BM>();  // 144 KiB at 128 rows
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<F32>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -741,11 +747,11 @@ hipError_t launch_ws(gemm_group& g, hipStream_t s) {
   int64_t total = 0;
   for (int i = 0; i < g.count; ++i) {
     g.p[i].block0 = (int32_t)total;
-    g.p[i].blocks = (int32_t)(((g.p[i].n + tiled::BN - 1) / tiled::BN) * ((g.p[i].m + wsk::BM - 1) / wsk::BM));
+    g.p[i].blocks = (int32_t)(((g.p[i].n + tiled::BN - 1) / tiled::BN) * ((g.p[i].m + BM - 1) / BM));
     total += (g.p[i].blocks + 7) / 8 * 8;
   }
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_ws<F32>), dim3((unsigned)total), dim3(64 * wsk::WAVES), lds_bytes, s, g);
+  hipLaunchKernelGGL((k_gemm_ws<F32, BM>), dim3((unsigned)total), dim3(64 * wsk::WAVES), lds_bytes, s, g);
   return hipGetLastError();
 }
 
@@ -798,7 +804,7 @@ hipError_t launch_tiled_group(gemm_group& g, int out_f32, int block_m, hipStream
     case 64:
       return out_f32 ? launch_tiled_bm<true, 64>(g, s) : launch_tiled_bm<false, 64>(g, s);
     case 128:
-      return out_f32 ? launch_ws<true>(g, s) : launch_ws<false>(g, s);
+      return out_f32 ? launch_ws<true, 128>(g, s) : launch_ws<false, 128>(g, s);
     default:
       return out_f32 ? launch_tiled_bm<true, 256>(g, s) : launch_tiled_bm<false, 256>(g, s);
   }
