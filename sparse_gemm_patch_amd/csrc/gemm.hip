@@ -586,18 +586,20 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < XB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int step, int stage) {
+  // Operands of one step: read by load_ops, consumed by mma.
+  int d0 = -1, d1 = -1;  // per 64-row half: 1 dense, 0 2:4, -1 past N
+  bf16x16 b[XB];
+  bf16x8 a0[8], a1[8];
+  int ix[8];
+  auto load_ops = [&](int step, int stage) {
     const uint8_t* cur = lds + stage * STAGE_BYTES;
-    const int d0 = hok0 ? ((tile_desc[hdesc0 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
-    const int d1 = hok1 ? ((tile_desc[hdesc1 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
-    bf16x16 b[XB];
+    d0 = hok0 ? ((tile_desc[hdesc0 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
+    d1 = hok1 ? ((tile_desc[hdesc1 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
 #pragma unroll
     for (int bm = 0; bm < XB; ++bm) {
       const int r = RW * wm + 16 * bm + r16;
       b[bm] = cat16(lds8(cur + r * 128 + ((q ^ xswz(r)) << 4)), lds8(cur + r * 128 + (((4 + q) ^ xswz(r)) << 4)));
     }
-    bf16x8 a0[8], a1[8];
-    int ix[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int dh = h ? d1 : d0;
@@ -617,6 +619,8 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
         ix[4 * h + 2] = ix[4 * h + 3] = (int)c.y;
       }
     }
+  };
+  auto mma = [&]() {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int dh = h ? d1 : d0;
@@ -640,12 +644,33 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
       }
     }
   };
+  // The two computing waves of a SIMD (wave w and w + 4) run half a step
+  // apart: waves 0-3 read step i and multiply it, waves 4-7 multiply step
+  // i - 1 (read in the previous step) and then read step i, so that one of
+  // them reads LDS while the other keeps the matrix unit busy.  Separate
+  // loops keep the compiler from holding both schedules' registers.
   int stage = 0;
-  for (int i = 0; i < nsteps; ++i) {
-    wait_copies_but(0);  // this wave's LDS reads of the previous step are done
-    barrier();           // step i is in `stage`
-    compute(i, stage);
-    stage = stage == 2 ? 0 : stage + 1;
+  if (wn == 0) {
+    for (int i = 0; i < nsteps; ++i) {
+      wait_copies_but(0);  // this wave's LDS reads of the previous step are done
+      barrier();           // step i is in `stage`
+      load_ops(i, stage);
+      mma();
+      stage = stage == 2 ? 0 : stage + 1;
+    }
+  } else if (nsteps > 0) {
+    wait_copies_but(0);
+    barrier();
+    load_ops(0, 0);
+    stage = 1;
+    for (int i = 1; i < nsteps; ++i) {
+      wait_copies_but(0);
+      barrier();
+      mma();
+      load_ops(i, stage);
+      stage = stage == 2 ? 0 : stage + 1;
+    }
+    mma();
   }
   void* __restrict__ y = P.y;
   const int64_t ldy = P.ldy;
@@ -759,7 +784,7 @@ hipError_t launch_ws(gemm_group& g, hipStream_t s) {
 // (smaller blocks move more LDS bytes per flop), times the K steps.
 double block_cost(int bm, int64_t k) {
   // measured in whole rounds on the 8192x2048 and 4096x4096 products at M = 4096
-  const double eff = bm == 256 ? 1.0 : bm == 128 ? 0.93 : 0.68;
+  const double eff = bm == 256 ? 1.0 : bm == 128 ? 0.96 : 0.68;
   return bm / 256.0 / eff * (double)(k / 64);
 }
 }  // namespace
