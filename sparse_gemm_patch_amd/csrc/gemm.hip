@@ -187,24 +187,25 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
 }
 
 // ------------------------------------------------------------------------
-// Tiled kernel for prefill-sized M.
+// Tiled kernel for prefill-sized M (256 and 64 X rows per block; 128-row
+// blocks run on k_gemm_ws below).
 //
 // Workgroup = 8 waves in a 2 x 4 grid; the block of Y^T is 256 W rows (n) x
-// BM X rows (m), BM = 256, 128 or 64.  Wave (wn, wm) owns W rows 128 wn .. +127
-// (8 row blocks of 16, in two 64-row groups that each lie in one tile row) and
-// X rows BM/4 wm .. +BM/4-1 (BM/64 column blocks): up to 8 x 4 accumulator
-// blocks of 16 x 16, 128 fp32 accumulators per lane, two waves per SIMD.  K
-// advances 64 at a time; a step never crosses a tile.  The smaller BM exist
-// for shapes whose 256 x 256 blocks would leave CUs idle: they cost more LDS
-// traffic per flop, but no block has to be split along K (a cross-workgroup
-// reduction needs device-scope fences, which on this chip write back the
-// whole L2 of an XCD).
+// BM X rows (m).  Wave (wn, wm) owns W rows 128 wn .. +127 (8 row blocks of
+// 16, in two 64-row groups that each lie in one tile row) and X rows
+// BM/4 wm .. +BM/4-1 (BM/64 column blocks): up to 8 x 4 accumulator blocks of
+// 16 x 16, 128 fp32 accumulators per lane, two waves per SIMD.  K advances 64
+// at a time; a step never crosses a tile.  The smaller blocks exist for
+// shapes whose 256 x 256 blocks would leave CUs idle: no block is split along
+// K (a cross-workgroup reduction needs device-scope fences, which on this chip
+// write back the whole L2 of an XCD).
 //
-// What bounds this kernel on MI355X is LDS traffic: per step a CU writes
-// 50 KiB (2:4) to 64 KiB (dense) into LDS and its waves read 136 to 192 KiB
-// back, at 256 bytes per clock for conflict-free 16-byte reads, next to 64
-// (2:4) to 128 (dense) MFMAs of 16 x 16 x 64 per SIMD at 16 clocks each.
-// Every LDS access pattern below runs at the full rate.
+// Per 256 x 256 step a CU copies 50 KiB (2:4) to 64 KiB (dense) into LDS,
+// through a fill path of about 64 bytes per clock, its waves read 136 to
+// 192 KiB back at up to 256 bytes per clock, and each SIMD runs 64 (2:4) to
+// 128 (dense) smfmacs of 16 clocks.  Measured inside the kernel, a step takes
+// about three times its smfmac time: the copy issue, the LDS read burst after
+// the barrier and the barrier itself do not overlap well.
 //
 // LDS holds two stages of BM * 128 + 32 KiB:
 //   X  BM rows x 128 B; 16-byte chunk c of row r at position c ^ (r & 7).
@@ -216,14 +217,15 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
 //      of codes at +4 KiB, 8 bytes per lane (one code word per block).  Lane l
 //      reads bytes 16 l .. 16 l + 15 of a block (or 8 l .. 8 l + 7 of the
 //      codes): consecutive lanes, consecutive addresses.
-// Every wave copies its share of each step (BM/8 X rows and a quarter of the
-// W data) straight from global memory into LDS with
-// global_load_lds, one step ahead, then waits for its own copies before the
-// step's barrier.  The copies are issued from inline assembly (which saves and
-// restores M0, the LDS address register): the compiler cannot tell that they
-// target the other stage, and as builtins every LDS read after them would wait
-// for them to land.  The kernel issues no other vector-memory loads, so the
-// explicit waits are the only ones these copies need.
+// Waves 4-7 copy the whole next step (a quarter of the X rows and one W group
+// each) straight from global memory into LDS with global_load_lds, then wait
+// for their copies before the step's barrier; waves 0-3 only compute, so they
+// never stall on the fill path.  The copies are issued from inline assembly
+// (which saves and restores M0, the LDS address register): the compiler
+// cannot tell that they target the other stage, and as builtins every LDS read
+// after them would wait for them to land.  The kernel issues no other
+// vector-memory loads, so the explicit waits are the only ones these copies
+// need.
 // ------------------------------------------------------------------------
 namespace tiled {
 constexpr int BN = 256, BK = 64;
