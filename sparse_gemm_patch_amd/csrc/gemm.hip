@@ -286,6 +286,59 @@ __device__ __forceinline__ void block_origin(int64_t n, int64_t m, int bid, int6
 // otherwise assumed to alias Y, which forces vector loads).
 typedef const __attribute__((address_space(4))) int32_t* const_desc_ptr;
 
+// Epilogue of a computing wave: its block of Y^T, W rows wrow0 .. +127 (two
+// 64-row halves) by X rows mrow0 .. +RW-1, where lane (q, r16) of accumulator
+// block (bn, bm) holds rows n = 16 bn + 4 q .. +3 of column m = 16 bm + r16.
+// For bf16 Y each half goes through `region` (RW x 128 bytes of LDS that no
+// other wave touches; 16-byte chunk c of row r at position c ^ (r & 7)) and
+// leaves as 16-byte stores, eight whole 128-byte row segments of Y per
+// instruction.  Written straight from the accumulators, each store would
+// cover 16 rows x 32 bytes, and the partial lines cost about a sixth of the
+// kernel time on the 8192 x 2048 product at M = 4096.  fp32 Y is stored
+// directly (16 bytes per lane).
+template <bool F32, int RW, int XB>
+__device__ __forceinline__ void store_block(const f32x4 (&acc)[8][XB], uint8_t* region, void* __restrict__ y,
+                                            int64_t ldy, int64_t m, int64_t mrow0, int64_t wrow0, bool hok0,
+                                            bool hok1, int lane) {
+  const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h == 0 ? !hok0 : !hok1) continue;
+    if (F32) {
+#pragma unroll
+      for (int bm = 0; bm < XB; ++bm) {
+        const int64_t mm = mrow0 + 16 * bm + r16;
+        if (mm >= m) continue;
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const f32x4 v = acc[4 * h + b4][bm];
+          store4<true>(y, ldy, mm, wrow0 + 64 * h + 16 * b4 + 4 * q, v[0], v[1], v[2], v[3]);
+        }
+      }
+      continue;
+    }
+#pragma unroll
+    for (int bm = 0; bm < XB; ++bm)
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const f32x4 v = acc[4 * h + b4][bm];
+        const int r = 16 * bm + r16, c = 2 * b4 + (q >> 1);
+        uint2 w;
+        w.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        w.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<uint2*>(region + r * 128 + ((c ^ (r & 7)) << 4) + ((q & 1) << 3)) = w;
+      }
+#pragma unroll
+    for (int j = 0; j < RW / 8; ++j) {
+      const int r = 8 * j + (lane >> 3), c = lane & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(region + r * 128 + ((c ^ (r & 7)) << 4));
+      const int64_t mm = mrow0 + r;
+      if (mm < m)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(y) + mm * ldy + wrow0 + 64 * h + 8 * c) = v;
+    }
+  }
+}
+
 template <bool F32, int BM>
 __global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
   using namespace tiled;
@@ -445,48 +498,38 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
     compute(i, i & 1);
   }
 
-  // epilogue: per block, lane holds rows n = 4 q + (0..3) of column m = r16
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (h == 0 ? !hok0 : !hok1) continue;
-#pragma unroll
-    for (int bm = 0; bm < XB; ++bm) {
-      const int64_t mm = m0 + BM / 4 * wm + 16 * bm + r16;
-      if (mm >= m) continue;
-#pragma unroll
-      for (int b4 = 0; b4 < 4; ++b4) {
-        const int bn = 4 * h + b4;
-        const f32x4 v = acc[bn][bm];
-        store4<F32>(y, ldy, mm, wrow0 + 16 * bn + 4 * q, v[0], v[1], v[2], v[3]);
-      }
-    }
-  }
+  // After the last barrier every wave is done with step nsteps - 2, and no copy
+  // targets its stage any more: each wave stages its Y block there.
+  static_assert(8 * (BM / 4) * 128 <= STAGE_BYTES, "Y staging fits one stage");
+  uint8_t* region = lds + (nsteps & 1) * STAGE_BYTES + wave * (BM / 4 * 128);
+  store_block<F32, BM / 4, XB>(acc, region, y, ldy, m, m0 + BM / 4 * wm, wrow0, hok0, hok1, lane);
 }
 
 // ------------------------------------------------------------------------
-// Warp-specialised kernel for 128 X rows per block: 12 waves.  Waves 0-7
-// compute exactly as in k_gemm_tiled with BM = 128 (2 x 4 grid, 128 W rows x 32
-// X rows each, two per SIMD); waves 8-11 (one per SIMD) only copy, two steps
-// ahead through three 48 KiB LDS stages.  A wave that issues copies stalls
-// while the per-CU fill path drains; here no computing wave ever does, and
-// the third stage hides the copies' latency.
+// Warp-specialised kernel for 128 X rows per block, and for 64 when the grid
+// gives each CU at most one workgroup: 12 waves.  Waves 0-7 compute exactly as
+// in k_gemm_tiled (2 x 4 grid, 128 W rows x BM/4 X rows each, two per SIMD);
+// waves 8-11 (one per SIMD) only copy, two steps ahead through three LDS
+// stages (48 KiB each at 128 rows, 40 at 64).  A wave that issues copies
+// stalls while the per-CU fill path drains; here no computing wave ever does,
+// and the third stage hides the copies' latency.
 // ------------------------------------------------------------------------
 namespace wsk {
 constexpr int STAGES = 3, WAVES = 12;
 template <int BM> constexpr int stage_bytes() { return BM * 128 + 4 * tiled::G_BYTES; }  // 48 KiB at 128 rows
 }  // namespace wsk
 
-// Wait until at most n (XC, XC + 6 or XC + 8 with XC = 2 or 4) of this wave's
-// copies are outstanding, and for its LDS reads.
+// Wait until at most n of this wave's copies are outstanding, and for its LDS
+// reads.  n is the copy count of one step: XC (2 or 4) X copies plus 0, 6 or 8
+// W copies.
 __device__ __forceinline__ void wait_copies_but(int n) {
+#define PATCH_WAIT_CASE(c) \
+  case c: asm volatile("s_waitcnt vmcnt(" #c ") lgkmcnt(0)" ::: "memory"); break;
   switch (n) {
-    case 12: asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory"); break;
-    case 10: asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory"); break;
+    PATCH_WAIT_CASE(12) PATCH_WAIT_CASE(10) PATCH_WAIT_CASE(8) PATCH_WAIT_CASE(4) PATCH_WAIT_CASE(2)
     default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
   }
+#undef PATCH_WAIT_CASE
 }
 
 template <bool F32, int BM>
@@ -674,23 +717,12 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
     }
     mma();
   }
-  void* __restrict__ y = P.y;
-  const int64_t ldy = P.ldy;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (h == 0 ? !hok0 : !hok1) continue;
-#pragma unroll
-    for (int bm = 0; bm < XB; ++bm) {
-      const int64_t mm = m0 + RW * wm + 16 * bm + r16;
-      if (mm >= m) continue;
-#pragma unroll
-      for (int b4 = 0; b4 < 4; ++b4) {
-        const int bn = 4 * h + b4;
-        const f32x4 v = acc[bn][bm];
-        store4<F32>(y, ldy, mm, wrow0 + 16 * bn + 4 * q, v[0], v[1], v[2], v[3]);
-      }
-    }
-  }
+  // After the last barrier only the stage of step nsteps - 1 is still read, and
+  // no copy is in flight: the stage step nsteps would have used holds the
+  // computing waves' Y blocks (8 x RW x 128 bytes).
+  static_assert(8 * RW * 128 <= STAGE_BYTES, "Y staging fits one stage");
+  uint8_t* region = lds + (nsteps % STAGES) * STAGE_BYTES + wave * (RW * 128);
+  store_block<F32, RW, XB>(acc, region, P.y, P.ldy, m, m0 + RW * wm, wrow0, hok0, hok1, lane);
 }
 
 template <bool F32>
@@ -763,7 +795,8 @@ hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
 
 template <bool F32, int BM>
 hipError_t launch_ws(gemm_group& g, hipStream_t s) {
-  constexpr int lds_bytes = wsk::STAGES * wsk::stage_bytes<BM>();  // 144 KiB at 128 rows
+  constexpr int lds_bytes = wsk::STAGES * wsk::stage_bytes<BM>();  // 144 KiB at 128 rows, 120 at 64
+  static_assert(lds_bytes <= 160 * 1024, "LDS of one workgroup");
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM>),
@@ -780,6 +813,14 @@ hipError_t launch_ws(gemm_group& g, hipStream_t s) {
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL((k_gemm_ws<F32, BM>), dim3((unsigned)total), dim3(64 * wsk::WAVES), lds_bytes, s, g);
   return hipGetLastError();
+}
+
+// Workgroups of a launch at block height bm, each product padded to a multiple of 8.
+int64_t padded_blocks(const gemm_group& g, int bm) {
+  int64_t total = 0;
+  for (int i = 0; i < g.count; ++i)
+    total += (((g.p[i].n + tiled::BN - 1) / tiled::BN) * ((g.p[i].m + bm - 1) / bm) + 7) / 8 * 8;
+  return total;
 }
 
 // Relative cost of one workgroup: block height over its measured efficiency
@@ -829,6 +870,11 @@ hipError_t launch_tiled_group(gemm_group& g, int out_f32, int block_m, hipStream
   const int bm = block_m > 0 ? block_m : tiled_block_m(g);
   switch (bm) {
     case 64:
+      // Two 64-row k_gemm_tiled workgroups share a CU and overlap each other;
+      // when the grid gives each CU at most one, the warp-specialised kernel
+      // (copies two steps ahead) is 15-20% faster (512 x 2048 at M = 4096).
+      if (padded_blocks(g, 64) <= 256)
+        return out_f32 ? launch_ws<true, 64>(g, s) : launch_ws<false, 64>(g, s);
       return out_f32 ? launch_tiled_bm<true, 64>(g, s) : launch_tiled_bm<false, 64>(g, s);
     case 128:
       return out_f32 ? launch_ws<true, 128>(g, s) : launch_ws<false, 128>(g, s);

@@ -248,6 +248,27 @@ def test_tiled_block_rows(P, block_m, tn, tk, frac):
     y16 = pw.gemm(x, out_dtype=torch.bfloat16, kernel="tiled", block_m=block_m)
     assert O.rel_error(y_host(y32), ref) <= 1e-4
     assert O.rel_error(y_host(y16), ref) <= TOL
+    # bf16 Y leaves through an LDS staging buffer, fp32 Y straight from the
+    # accumulators: the two must agree to the last bit after rounding
+    assert torch.equal(y16, y32.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("m,n", [(5500, 640), (4096, 1024)])
+def test_tiled_64_rows_both_kernels(P, m, n):
+    """64-row blocks run on the warp-specialised kernel when the grid has at most 256 workgroups
+    (4096 x 1024: 4 x 64) and on two-per-CU k_gemm_tiled workgroups above (5500 x 640: 3 x 86)."""
+    prob = I.make_problem("bm64", m, n, 512, 128, 64, frac=0.6, cfg=51)
+    pw = pack_problem(P, prob)
+    x = dev_u16(prob.x)
+    y32 = pw.gemm(x, out_dtype=torch.float32, kernel="tiled", block_m=64)
+    y16 = pw.gemm(x, out_dtype=torch.bfloat16, kernel="tiled", block_m=64)
+    y256 = pw.gemm(x, out_dtype=torch.float32, kernel="tiled", block_m=256)
+    torch.cuda.synchronize()
+    assert torch.equal(y32, y256)  # same K order in every block height
+    assert torch.equal(y16, y32.to(torch.bfloat16))
+    rows = np.r_[0:70, m - 70:m]
+    ref = O.gemm_ref(prob.x[rows], O.masked_weight(prob.w, prob.mask))
+    assert O.rel_error(y_host(y32)[rows], ref) <= 1e-4
 
 
 @pytest.mark.parametrize("block_m", [256, 128, 64])
