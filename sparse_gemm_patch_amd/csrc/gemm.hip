@@ -291,10 +291,12 @@ typedef const __attribute__((address_space(4))) int32_t* const_desc_ptr;
 // block (bn, bm) holds rows n = 16 bn + 4 q .. +3 of column m = 16 bm + r16.
 // For bf16 Y each half goes through `region` (RW x 128 bytes of LDS that no
 // other wave touches; 16-byte chunk c of row r at position c ^ (r & 7)) and
-// leaves as 16-byte stores, eight whole 128-byte row segments of Y per
-// instruction.  Written straight from the accumulators, each store would
-// cover 16 rows x 32 bytes, and the partial lines cost about a sixth of the
-// kernel time on the 8192 x 2048 product at M = 4096.  fp32 Y is stored
+// leaves as 16-byte non-temporal stores, eight whole 128-byte row segments of
+// Y per instruction.  Written straight from the accumulators, each store
+// would cover 16 rows x 32 bytes: on the 8192 x 2048 product at M = 4096 that
+// costs 5% more, and as non-temporal stores twice the kernel time.  Whole
+// lines stored non-temporally stream out while other workgroups compute
+// (2-8% faster than ordinary stores of the same lines).  fp32 Y is stored
 // directly (16 bytes per lane).
 template <bool F32, int RW, int XB>
 __device__ __forceinline__ void store_block(const f32x4 (&acc)[8][XB], uint8_t* region, void* __restrict__ y,
@@ -331,19 +333,20 @@ __device__ __forceinline__ void store_block(const f32x4 (&acc)[8][XB], uint8_t* 
 #pragma unroll
     for (int j = 0; j < RW / 8; ++j) {
       const int r = 8 * j + (lane >> 3), c = lane & 7;
-      const uint4 v = *reinterpret_cast<const uint4*>(region + r * 128 + ((c ^ (r & 7)) << 4));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(region + r * 128 + ((c ^ (r & 7)) << 4));
       const int64_t mm = mrow0 + r;
       if (mm < m)
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(y) + mm * ldy + wrow0 + 64 * h + 8 * c) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(y) + mm * ldy + wrow0 + 64 * h + 8 * c));
     }
   }
 }
 
+// One output block of k_gemm_tiled: workgroup slot `slot` of the launch.
 template <bool F32, int BM>
-__global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
+__device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
   using namespace tiled;
   int local;
-  const int pi = find_problem(g, blockIdx.x, local);
+  const int pi = find_problem(g, slot, local);
   if (pi < 0) return;
   const gemm_problem& P = g.p[pi];
   const const_desc_ptr tile_desc = (const_desc_ptr)P.tile_desc;
@@ -359,7 +362,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
-  const int lane = threadIdx.x & 63;
+  // Opaque per block, so that the compiler recomputes the lane-dependent
+  // offsets for every block instead of holding them across the block loop.
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave >> 2, wm = wave & 3;
   const int q = lane >> 4, r16 = lane & 15;
@@ -505,6 +511,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
   store_block<F32, BM / 4, XB>(acc, region, y, ldy, m, m0 + BM / 4 * wm, wrow0, hok0, hok1, lane);
 }
 
+// Persistent: each workgroup takes slots blockIdx.x, + gridDim.x, ...  The
+// grid is a multiple of 8, so every slot stays on the XCD its number maps to,
+// and a block's Y stores drain while the same workgroup copies and multiplies
+// its next block.  The barrier between blocks keeps the next block's first
+// copies off LDS that slower waves still read.
+template <bool F32, int BM>
+__global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
+  for (int slot = blockIdx.x; slot < g.total; slot += gridDim.x) {
+    tiled_block<F32, BM>(g, slot);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
 // ------------------------------------------------------------------------
 // Warp-specialised kernel for 128 X rows per block, and for 64 when the grid
 // gives each CU at most one workgroup: 12 waves.  Waves 0-7 compute exactly as
@@ -532,8 +551,9 @@ __device__ __forceinline__ void wait_copies_but(int n) {
 #undef PATCH_WAIT_CASE
 }
 
+// One output block of k_gemm_ws: workgroup slot `slot` of the launch.
 template <bool F32, int BM>
-__global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
+__device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
   using namespace wsk;
   using tiled::G_BYTES;
   constexpr int X_BYTES = BM * 128, STAGE_BYTES = stage_bytes<BM>();
@@ -541,7 +561,7 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
   constexpr int XC = RW / 8;   // X copies per copy wave
   constexpr int XB = RW / 16;  // X blocks of 16 rows per compute wave
   int local;
-  const int pi = find_problem(g, blockIdx.x, local);
+  const int pi = find_problem(g, slot, local);
   if (pi < 0) return;
   const gemm_problem& P = g.p[pi];
   const const_desc_ptr tile_desc = (const_desc_ptr)P.tile_desc;
@@ -550,7 +570,10 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
-  const int lane = threadIdx.x & 63;
+  // Opaque per block, so that the compiler recomputes the lane-dependent
+  // offsets for every block instead of holding them across the block loop.
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t n0, m0;
   block_origin<BM>(n, m, local, n0, m0);
@@ -725,6 +748,15 @@ __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
   store_block<F32, RW, XB>(acc, region, P.y, P.ldy, m, m0 + RW * wm, wrow0, hok0, hok1, lane);
 }
 
+// Persistent like k_gemm_tiled.
+template <bool F32, int BM>
+__global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
+  for (int slot = blockIdx.x; slot < g.total; slot += gridDim.x) {
+    ws_block<F32, BM>(g, slot);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
 template <bool F32>
 __global__ void k_fill_zero_y(void* y, int64_t m, int64_t n, int64_t ldy) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -770,6 +802,24 @@ hipError_t launch_stream_group(gemm_group& g, int out_f32, hipStream_t s) {
 }
 
 namespace {
+// Grid of a persistent launch: the workgroups the device holds at once
+// (queried once per device into cache[device]), rounded down to a multiple of
+// 8, and never more than the launch's slots.  -1 if the device cannot be
+// queried.
+int persistent_grid(const void* kernel, int threads, int lds_bytes, int* cache, int64_t slots) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  if (cache[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds_bytes) != hipSuccess)
+      return -1;
+    const int r = cus * (per_cu > 0 ? per_cu : 1) / 8 * 8;
+    cache[dev] = r > 8 ? r : 8;
+  }
+  return slots < cache[dev] ? (int)slots : cache[dev];
+}
+
 template <bool F32, int BM>
 hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
   constexpr int lds_bytes = tiled::STAGES * tiled::stage_bytes<BM>();  // above 64 KiB: opt in, once
@@ -789,7 +839,11 @@ hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
     total += (g.p[i].blocks + 7) / 8 * 8;
   }
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_tiled<F32, BM>), dim3((unsigned)total), dim3(512), lds_bytes, s, g);
+  static int resident[64] = {};
+  const int grid = persistent_grid(reinterpret_cast<const void*>(&k_gemm_tiled<F32, BM>), 512, lds_bytes, resident, total);
+  if (grid < 0) return hipErrorInvalidDevice;
+  g.total = (int32_t)total;
+  hipLaunchKernelGGL((k_gemm_tiled<F32, BM>), dim3((unsigned)grid), dim3(512), lds_bytes, s, g);
   return hipGetLastError();
 }
 
@@ -811,7 +865,12 @@ hipError_t launch_ws(gemm_group& g, hipStream_t s) {
     total += (g.p[i].blocks + 7) / 8 * 8;
   }
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_ws<F32, BM>), dim3((unsigned)total), dim3(64 * wsk::WAVES), lds_bytes, s, g);
+  static int resident[64] = {};
+  const int grid =
+      persistent_grid(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM>), 64 * wsk::WAVES, lds_bytes, resident, total);
+  if (grid < 0) return hipErrorInvalidDevice;
+  g.total = (int32_t)total;
+  hipLaunchKernelGGL((k_gemm_ws<F32, BM>), dim3((unsigned)grid), dim3(64 * wsk::WAVES), lds_bytes, s, g);
   return hipGetLastError();
 }
 

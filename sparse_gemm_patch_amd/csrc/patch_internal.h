@@ -69,7 +69,7 @@ struct gemm_problem {
 };
 struct gemm_group {
   int32_t count;
-  int32_t _pad;
+  int32_t total;  // workgroup slots of the whole launch (tiled kernels)
   gemm_problem p[PATCH_MAX_GROUP];
 };
 // The product of handle w with X [m][ldx] into Y [m][ldy] (block fields unset).
