@@ -253,6 +253,20 @@ def test_tiled_block_rows(P, block_m, tn, tk, frac):
     assert torch.equal(y16, y32.to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("tn,tk,k", [(64, 64, 4224), (128, 128, 8448)])
+def test_tiled_more_than_64_tile_columns(P, tn, tk, k):
+    """66 tile columns: the tiled kernel holds descriptors 64 columns at a time and must move
+    to the next window in the middle of a block."""
+    prob = I.make_problem("win", 300, 256, k, tn, tk, frac=0.5, cfg=52)
+    pw = pack_problem(P, prob)
+    x = dev_u16(prob.x)
+    ys = [pw.gemm(x, out_dtype=torch.float32, kernel="tiled", block_m=b) for b in (256, 128, 64)]
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+    ref = O.gemm_ref(prob.x, O.masked_weight(prob.w, prob.mask))
+    assert O.rel_error(y_host(ys[0]), ref) <= 1e-4
+
+
 @pytest.mark.parametrize("m,n", [(5500, 640), (4096, 1024)])
 def test_tiled_64_rows_both_kernels(P, m, n):
     """64-row blocks run on the warp-specialised kernel when the grid has at most 256 workgroups
