@@ -270,9 +270,9 @@ __device__ __forceinline__ int xswz(int r) { return r & 7; }
 // X in that XCD's L2.
 // bid: the workgroup's index inside its product, whose first workgroup is a
 // multiple of 8 in the launch (so bid % 8 is still its XCD).
-template <int BM>
+template <int BM, int BN>
 __device__ __forceinline__ void block_origin(int64_t n, int64_t m, int bid, int64_t& n0, int64_t& m0) {
-  using namespace tiled;
+  using tiled::GROUP_N;
   const int nbn = (int)((n + BN - 1) / BN), nbm = (int)((m + BM - 1) / BM);
   const int total = nbn * nbm;
   const int xcd = bid & 7, local = bid >> 3, base = total >> 3, rem = total & 7;
@@ -304,10 +304,10 @@ __device__ __forceinline__ int32_t desc_window(const_desc_ptr tile_desc, int64_t
   return c < tiles_k ? tile_desc[row_base + c] : 0;
 }
 
-// Epilogue of a computing wave: its block of Y^T, W rows wrow0 .. +127 (two
-// 64-row halves) by X rows mrow0 .. +RW-1, where lane (q, r16) of accumulator
-// block (bn, bm) holds rows n = 16 bn + 4 q .. +3 of column m = 16 bm + r16.
-// For bf16 Y each half goes through `region` (RW x 128 bytes of LDS that no
+// Epilogue of a computing wave: its block of Y^T, W rows wrow0 .. +64 GW - 1
+// (GW 64-row groups) by X rows mrow0 .. +RW-1, where lane (q, r16) of
+// accumulator block (bn, bm) holds rows n = 16 bn + 4 q .. +3 of column
+// m = 16 bm + r16.  For bf16 Y each group goes through `region` (RW x 128 bytes of LDS that no
 // other wave touches; 16-byte chunk c of row r at position c ^ (r & 7)) and
 // leaves as 16-byte non-temporal stores, eight whole 128-byte row segments of
 // Y per instruction.  Written straight from the accumulators, each store
@@ -316,14 +316,14 @@ __device__ __forceinline__ int32_t desc_window(const_desc_ptr tile_desc, int64_t
 // lines stored non-temporally stream out while other workgroups compute
 // (2-8% faster than ordinary stores of the same lines).  fp32 Y is stored
 // directly (16 bytes per lane).
-template <bool F32, int RW, int XB>
-__device__ __forceinline__ void store_block(const f32x4 (&acc)[8][XB], uint8_t* region, void* __restrict__ y,
-                                            int64_t ldy, int64_t m, int64_t mrow0, int64_t wrow0, bool hok0,
-                                            bool hok1, int lane) {
+template <bool F32, int RW, int XB, int GW>
+__device__ __forceinline__ void store_block(const f32x4 (&acc)[4 * GW][XB], uint8_t* region, void* __restrict__ y,
+                                            int64_t ldy, int64_t m, int64_t mrow0, int64_t wrow0,
+                                            const bool (&hok)[GW], int lane) {
   const int q = lane >> 4, r16 = lane & 15;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (h == 0 ? !hok0 : !hok1) continue;
+  for (int h = 0; h < GW; ++h) {
+    if (!hok[h]) continue;
     if (F32) {
 #pragma unroll
       for (int bm = 0; bm < XB; ++bm) {
@@ -388,7 +388,7 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
   const int wn = wave >> 2, wm = wave & 3;
   const int q = lane >> 4, r16 = lane & 15;
   int64_t n0, m0;
-  block_origin<BM>(n, m, local, n0, m0);
+  block_origin<BM, BN>(n, m, local, n0, m0);
   const int nsteps = (int)(k / BK);
   const int ks = tk == 128;           // 64-wide K steps per tile column: 1 << ks
   const int ns = tn == 128 ? 7 : 6;   // log2(TN)
@@ -547,7 +547,8 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
   // targets its stage any more: each wave stages its Y block there.
   static_assert(8 * (BM / 4) * 128 <= STAGE_BYTES, "Y staging fits one stage");
   uint8_t* region = lds + (nsteps & 1) * STAGE_BYTES + wave * (BM / 4 * 128);
-  store_block<F32, BM / 4, XB>(acc, region, y, ldy, m, m0 + BM / 4 * wm, wrow0, hok0, hok1, lane);
+  const bool hok[2] = {hok0, hok1};
+  store_block<F32, BM / 4, XB, 2>(acc, region, y, ldy, m, m0 + BM / 4 * wm, wrow0, hok, lane);
 }
 
 // Persistent: each workgroup takes slots blockIdx.x, + gridDim.x, ...  The
@@ -574,7 +575,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
 // ------------------------------------------------------------------------
 namespace wsk {
 constexpr int STAGES = 3, WAVES = 12;
-template <int BM> constexpr int stage_bytes() { return BM * 128 + 4 * tiled::G_BYTES; }  // 48 KiB at 128 rows
+template <int BM, int NG> constexpr int stage_bytes() { return BM * 128 + NG * tiled::G_BYTES; }
 }  // namespace wsk
 
 // Wait until at most n of this wave's copies are outstanding, and for its LDS
@@ -590,12 +591,15 @@ __device__ __forceinline__ void wait_copies_but(int n) {
 #undef PATCH_WAIT_CASE
 }
 
-// One output block of k_gemm_ws: workgroup slot `slot` of the launch.
-template <bool F32, int BM>
+// One output block of k_gemm_ws: workgroup slot `slot` of the launch; the
+// block is NG 64-row W groups (BN = 64 NG rows of W) by BM rows of X.
+template <bool F32, int BM, int NG>
 __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
   using namespace wsk;
   using tiled::G_BYTES;
-  constexpr int X_BYTES = BM * 128, STAGE_BYTES = stage_bytes<BM>();
+  static_assert(NG == 2 || NG == 4, "128 or 256 W rows per block");
+  constexpr int BN = 64 * NG, GW = NG / 2;  // GW: W groups per computing wave
+  constexpr int X_BYTES = BM * 128, STAGE_BYTES = stage_bytes<BM, NG>();
   constexpr int RW = BM / 4;   // X rows per copy wave and per compute wave
   constexpr int XC = RW / 8;   // X copies per copy wave
   constexpr int XB = RW / 16;  // X blocks of 16 rows per compute wave
@@ -615,14 +619,14 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
   asm volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t n0, m0;
-  block_origin<BM>(n, m, local, n0, m0);
+  block_origin<BM, BN>(n, m, local, n0, m0);
   const int nsteps = (int)(k / 64);
   const int ks = tk == 128;
   const int ns = tn == 128 ? 7 : 6;
   const int bt = tn >> 4;
 
   if (wave >= 8) {
-    // ---- copy waves: X rows 32 c .. 32 c + 31 and W group c (rows n0 + 64 c ..)
+    // ---- copy waves: X rows RW c .. RW c + RW - 1 and W group c (rows n0 + 64 c ..) if c < NG
     const int cw = wave - 8;
     const int64_t ldx = P.ldx;
     const uint8_t* xblk = reinterpret_cast<const uint8_t*>(P.x + m0 * ldx);
@@ -635,7 +639,7 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
       xoff[j] = (uint32_t)(((gm - m0) * ldx + 8 * ((lane & 7) ^ xswz(row))) * 2);
     }
     const int64_t gn0 = n0 + 64 * cw;
-    const bool g_ok = gn0 < n;
+    const bool g_ok = cw < NG && gn0 < n;
     const int64_t g_desc = (gn0 >> ns) * tiles_k;
     const int g_blk = (int)((gn0 & (tn - 1)) >> 4);
     const uint8_t* dsrc = reinterpret_cast<const uint8_t*>(P.dense_vals);
@@ -682,43 +686,48 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
     return;
   }
 
-  // ---- compute waves: W rows 128 wn .. +127, X rows 32 wm .. +31
+  // ---- compute waves: W groups GW wn .. GW wn + GW - 1, X rows RW wm .. +RW-1
   const int wn = wave >> 2, wm = wave & 3;
   const int q = lane >> 4, r16 = lane & 15;
-  const int64_t wrow0 = n0 + 128 * wn;
-  const bool hok0 = wrow0 < n, hok1 = wrow0 + 64 < n;
-  const int64_t hdesc0 = (wrow0 >> ns) * tiles_k, hdesc1 = ((wrow0 + 64) >> ns) * tiles_k;
-  f32x4 acc[8][XB];
+  const int64_t wrow0 = n0 + 64 * GW * wn;
+  bool hok[GW];
+  int64_t hdesc[GW];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int h = 0; h < GW; ++h) {
+    hok[h] = wrow0 + 64 * h < n;
+    hdesc[h] = ((wrow0 + 64 * h) >> ns) * tiles_k;
+  }
+  f32x4 acc[4 * GW][XB];
+#pragma unroll
+  for (int i = 0; i < 4 * GW; ++i)
 #pragma unroll
     for (int j = 0; j < XB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Operands of one step: read by load_ops, consumed by mma.
-  int d0 = -1, d1 = -1;  // per 64-row half: 1 dense, 0 2:4, -1 past N
+  int dg[GW];  // per 64-row group: 1 dense, 0 2:4, -1 past N
   bf16x16 b[XB];
-  bf16x8 a0[8], a1[8];
-  int ix[8];
+  bf16x8 a0[4 * GW], a1[4 * GW];
+  int ix[4 * GW];
   auto load_ops = [&](int step, int stage) {
     const uint8_t* cur = lds + stage * STAGE_BYTES;
-    d0 = hok0 ? ((tile_desc[hdesc0 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
-    d1 = hok1 ? ((tile_desc[hdesc1 + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
+#pragma unroll
+    for (int h = 0; h < GW; ++h)
+      dg[h] = hok[h] ? ((tile_desc[hdesc[h] + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
 #pragma unroll
     for (int bm = 0; bm < XB; ++bm) {
       const int r = RW * wm + 16 * bm + r16;
       b[bm] = cat16(lds8(cur + r * 128 + ((q ^ xswz(r)) << 4)), lds8(cur + r * 128 + (((4 + q) ^ xswz(r)) << 4)));
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int dh = h ? d1 : d0;
-      const uint8_t* gp = cur + X_BYTES + (2 * wn + h) * G_BYTES;
-      if (dh > 0) {
+    for (int h = 0; h < GW; ++h) {
+      const uint8_t* gp = cur + X_BYTES + (GW * wn + h) * G_BYTES;
+      if (dg[h] > 0) {
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) {
           a0[4 * h + b4] = lds8(gp + 2048 * b4 + lane * 16);
           a1[4 * h + b4] = lds8(gp + 2048 * b4 + 1024 + lane * 16);
           ix[4 * h + b4] = 0x44444444;
         }
-      } else if (dh == 0) {
+      } else if (dg[h] == 0) {
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) a0[4 * h + b4] = lds8(gp + 1024 * b4 + lane * 16);
         const uint2 c = *reinterpret_cast<const uint2*>(gp + 4096 + 8 * lane);
@@ -729,9 +738,8 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
   };
   auto mma = [&]() {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int dh = h ? d1 : d0;
-      if (dh < 0) continue;
+    for (int h = 0; h < GW; ++h) {
+      if (dg[h] < 0) continue;
 #pragma unroll
       for (int bm = 0; bm < XB; ++bm)
 #pragma unroll
@@ -740,7 +748,7 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
           acc[bn][bm] = b4 & 1 ? __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b[bm], acc[bn][bm], ix[bn], 0, 1)
                                : __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b[bm], acc[bn][bm], ix[bn], 0, 0);
         }
-      if (dh > 0) {
+      if (dg[h] > 0) {
 #pragma unroll
         for (int bm = 0; bm < XB; ++bm)
 #pragma unroll
@@ -784,14 +792,14 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
   // computing waves' Y blocks (8 x RW x 128 bytes).
   static_assert(8 * RW * 128 <= STAGE_BYTES, "Y staging fits one stage");
   uint8_t* region = lds + (nsteps % STAGES) * STAGE_BYTES + wave * (RW * 128);
-  store_block<F32, RW, XB>(acc, region, P.y, P.ldy, m, m0 + RW * wm, wrow0, hok0, hok1, lane);
+  store_block<F32, RW, XB, GW>(acc, region, P.y, P.ldy, m, m0 + RW * wm, wrow0, hok, lane);
 }
 
 // Persistent like k_gemm_tiled.
-template <bool F32, int BM>
+template <bool F32, int BM, int NG>
 __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
   for (int slot = blockIdx.x; slot < g.total; slot += gridDim.x) {
-    ws_block<F32, BM>(g, slot);
+    ws_block<F32, BM, NG>(g, slot);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
@@ -886,13 +894,14 @@ hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool F32, int BM>
+template <bool F32, int BM, int NG>
 hipError_t launch_ws(gemm_group& g, hipStream_t s) {
-  constexpr int lds_bytes = wsk::STAGES * wsk::stage_bytes<BM>();  // 144 KiB at 128 rows, 120 at 64
+  constexpr int BN = 64 * NG;
+  constexpr int lds_bytes = wsk::STAGES * wsk::stage_bytes<BM, NG>();  // 144 KiB at 128 x 256, 120 at 64 x 256
   static_assert(lds_bytes <= 160 * 1024, "LDS of one workgroup");
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM, NG>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -900,24 +909,23 @@ hipError_t launch_ws(gemm_group& g, hipStream_t s) {
   int64_t total = 0;
   for (int i = 0; i < g.count; ++i) {
     g.p[i].block0 = (int32_t)total;
-    g.p[i].blocks = (int32_t)(((g.p[i].n + tiled::BN - 1) / tiled::BN) * ((g.p[i].m + BM - 1) / BM));
+    g.p[i].blocks = (int32_t)(((g.p[i].n + BN - 1) / BN) * ((g.p[i].m + BM - 1) / BM));
     total += (g.p[i].blocks + 7) / 8 * 8;
   }
   if (total == 0) return hipSuccess;
   static int resident[64] = {};
   const int grid =
-      persistent_grid(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM>), 64 * wsk::WAVES, lds_bytes, resident, total);
+      persistent_grid(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM, NG>), 64 * wsk::WAVES, lds_bytes, resident, total);
   if (grid < 0) return hipErrorInvalidDevice;
   g.total = (int32_t)total;
-  hipLaunchKernelGGL((k_gemm_ws<F32, BM>), dim3((unsigned)grid), dim3(64 * wsk::WAVES), lds_bytes, s, g);
+  hipLaunchKernelGGL((k_gemm_ws<F32, BM, NG>), dim3((unsigned)grid), dim3(64 * wsk::WAVES), lds_bytes, s, g);
   return hipGetLastError();
 }
 
-// Workgroups of a launch at block height bm, each product padded to a multiple of 8.
-int64_t padded_blocks(const gemm_group& g, int bm) {
+// Workgroups of a launch of bn x bm blocks, each product padded to a multiple of 8.
+int64_t padded_blocks(const gemm_group& g, int bm, int bn) {
   int64_t total = 0;
-  for (int i = 0; i < g.count; ++i)
-    total += (((g.p[i].n + tiled::BN - 1) / tiled::BN) * ((g.p[i].m + bm - 1) / bm) + 7) / 8 * 8;
+  for (int i = 0; i < g.count; ++i) total += (((g.p[i].n + bn - 1) / bn) * ((g.p[i].m + bm - 1) / bm) + 7) / 8 * 8;
   return total;
 }
 
@@ -970,12 +978,16 @@ hipError_t launch_tiled_group(gemm_group& g, int out_f32, int block_m, hipStream
     case 64:
       // Two 64-row k_gemm_tiled workgroups share a CU and overlap each other;
       // when the grid gives each CU at most one, the warp-specialised kernel
-      // (copies two steps ahead) is 15-20% faster (512 x 2048 at M = 4096).
-      if (padded_blocks(g, 64) <= 256)
-        return out_f32 ? launch_ws<true, 64>(g, s) : launch_ws<false, 64>(g, s);
+      // (copies two steps ahead) is 15-20% faster (512 x 2048 at M = 4096),
+      // and when it would leave half the CUs idle, blocks of 128 W rows
+      // (twice the workgroups) are faster still.
+      if (padded_blocks(g, 64, 256) <= 128)
+        return out_f32 ? launch_ws<true, 64, 2>(g, s) : launch_ws<false, 64, 2>(g, s);
+      if (padded_blocks(g, 64, 256) <= 256)
+        return out_f32 ? launch_ws<true, 64, 4>(g, s) : launch_ws<false, 64, 4>(g, s);
       return out_f32 ? launch_tiled_bm<true, 64>(g, s) : launch_tiled_bm<false, 64>(g, s);
     case 128:
-      return out_f32 ? launch_ws<true, 128>(g, s) : launch_ws<false, 128>(g, s);
+      return out_f32 ? launch_ws<true, 128, 4>(g, s) : launch_ws<false, 128, 4>(g, s);
     default:
       return out_f32 ? launch_tiled_bm<true, 256>(g, s) : launch_tiled_bm<false, 256>(g, s);
   }

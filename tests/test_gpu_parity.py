@@ -267,10 +267,12 @@ def test_tiled_more_than_64_tile_columns(P, tn, tk, k):
     assert O.rel_error(y_host(ys[0]), ref) <= 1e-4
 
 
-@pytest.mark.parametrize("m,n", [(5500, 640), (4096, 1024)])
-def test_tiled_64_rows_both_kernels(P, m, n):
-    """64-row blocks run on the warp-specialised kernel when the grid has at most 256 workgroups
-    (4096 x 1024: 4 x 64) and on two-per-CU k_gemm_tiled workgroups above (5500 x 640: 3 x 86)."""
+@pytest.mark.parametrize("m,n", [(5500, 640), (4096, 1024), (4096, 512)])
+def test_tiled_64_rows_every_kernel(P, m, n):
+    """64-row blocks run on two-per-CU k_gemm_tiled workgroups when 256-row-wide blocks give more
+    than 256 workgroups (5500 x 640: 3 x 86), on the warp-specialised kernel when they give at most
+    256 (4096 x 1024: 4 x 64), and on its 128-row-wide form when they give at most 128
+    (4096 x 512: 2 x 64)."""
     prob = I.make_problem("bm64", m, n, 512, 128, 64, frac=0.6, cfg=51)
     pw = pack_problem(P, prob)
     x = dev_u16(prob.x)
