@@ -236,7 +236,6 @@ namespace tiled {
 constexpr int BN = 256, BK = 64;
 constexpr int G_BYTES = 64 * 128;          // 8 KiB per 64-row W group
 constexpr int STAGES = 2;
-constexpr int GROUP_N = 4;                 // block columns per group of the block order
 template <int BM> constexpr int x_bytes() { return BM * 128; }
 template <int BM> constexpr int stage_bytes() { return x_bytes<BM>() + 4 * G_BYTES; }
 }  // namespace tiled
@@ -265,22 +264,22 @@ __device__ __forceinline__ int xswz(int r) { return r & 7; }
 
 // Output block of this workgroup.  The dispatcher deals workgroup i to XCD
 // i % 8; renumbering so that each XCD owns a contiguous range of blocks, walked
-// in groups of GROUP_N block columns (m fastest inside a group), makes the
+// in groups of group_n block columns (m fastest inside a group), makes the
 // workgroups resident on one XCD cover a compact region and share their W and
-// X in that XCD's L2.
+// X in that XCD's L2 (group_n is chosen by the launch, see group_width).
 // bid: the workgroup's index inside its product, whose first workgroup is a
 // multiple of 8 in the launch (so bid % 8 is still its XCD).
 template <int BM, int BN>
-__device__ __forceinline__ void block_origin(int64_t n, int64_t m, int bid, int64_t& n0, int64_t& m0) {
-  using tiled::GROUP_N;
+__device__ __forceinline__ void block_origin(int64_t n, int64_t m, int bid, int group_n, int64_t& n0,
+                                             int64_t& m0) {
   const int nbn = (int)((n + BN - 1) / BN), nbm = (int)((m + BM - 1) / BM);
   const int total = nbn * nbm;
   const int xcd = bid & 7, local = bid >> 3, base = total >> 3, rem = total & 7;
   const int id = xcd < rem ? xcd * (base + 1) + local : rem * (base + 1) + (xcd - rem) * base + local;
-  const int per_group = GROUP_N * nbm;
+  const int per_group = group_n * nbm;
   const int group = id / per_group, in_group = id % per_group;
-  const int first = group * GROUP_N;
-  const int width = nbn - first < GROUP_N ? nbn - first : GROUP_N;
+  const int first = group * group_n;
+  const int width = nbn - first < group_n ? nbn - first : group_n;
   n0 = (int64_t)(first + in_group % width) * BN;
   m0 = (int64_t)(in_group / width) * BM;
 }
@@ -388,7 +387,7 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
   const int wn = wave >> 2, wm = wave & 3;
   const int q = lane >> 4, r16 = lane & 15;
   int64_t n0, m0;
-  block_origin<BM, BN>(n, m, local, n0, m0);
+  block_origin<BM, BN>(n, m, local, P.group_n, n0, m0);
   const int nsteps = (int)(k / BK);
   const int ks = tk == 128;           // 64-wide K steps per tile column: 1 << ks
   const int ns = tn == 128 ? 7 : 6;   // log2(TN)
@@ -619,7 +618,7 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
   asm volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t n0, m0;
-  block_origin<BM, BN>(n, m, local, n0, m0);
+  block_origin<BM, BN>(n, m, local, P.group_n, n0, m0);
   const int nsteps = (int)(k / 64);
   const int ks = tk == 128;
   const int ns = tn == 128 ? 7 : 6;
@@ -831,6 +830,9 @@ gemm_problem make_problem(const patch_weight* w, const uint16_t* x, int64_t m, i
   p.ldy = ldy;
   p.tn = w->tn;
   p.tk = w->tk;
+  const double tiles = (double)(w->n_dense + w->n_sparse);
+  p.w_bytes = tiles > 0 ? (float)((2.0 * w->n_dense + 1.125 * w->n_sparse) / tiles) : 2.0f;
+  p.group_n = 4;
   return p;
 }
 
@@ -867,6 +869,33 @@ int persistent_grid(const void* kernel, int threads, int lds_bytes, int* cache, 
   return slots < cache[dev] ? (int)slots : cache[dev];
 }
 
+// The workgroups resident on one XCD (per_xcd of them) take consecutive
+// block numbers of the walk, so a round of them covers about w block columns
+// by per_xcd / w block rows, and that XCD's L2 fetches those blocks' X rows
+// and W rows over the whole K once per round: per_xcd / w * (bm K 2 bytes) +
+// w * (bn K w_bytes).  Each product gets the power-of-two width (at most its
+// block columns) that minimises it; FETCH_SIZE counts on MI355X follow this
+// model within a few per cent.  The time does not depend on it (the L2 hides
+// these fetches), only the memory traffic does.
+void group_width(gemm_group& g, int bm, int bn, int per_xcd) {
+  for (int i = 0; i < g.count; ++i) {
+    gemm_problem& p = g.p[i];
+    const int64_t nbn = (p.n + bn - 1) / bn;
+    const double xrow = 2.0 * bm * (double)p.k, wcol = (double)p.w_bytes * bn * (double)p.k;
+    int best = 1;
+    double best_b = 0;
+    for (int w = 1; w <= 32 && w <= nbn; w *= 2) {
+      const double rows = per_xcd / w > 1 ? (double)(per_xcd / w) : 1.0;
+      const double b = rows * xrow + w * wcol;
+      if (w == 1 || b < best_b) {
+        best = w;
+        best_b = b;
+      }
+    }
+    p.group_n = best;
+  }
+}
+
 template <bool F32, int BM>
 hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
   constexpr int lds_bytes = tiled::STAGES * tiled::stage_bytes<BM>();  // above 64 KiB: opt in, once
@@ -890,6 +919,7 @@ hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
   const int grid = persistent_grid(reinterpret_cast<const void*>(&k_gemm_tiled<F32, BM>), 512, lds_bytes, resident, total);
   if (grid < 0) return hipErrorInvalidDevice;
   g.total = (int32_t)total;
+  group_width(g, BM, tiled::BN, grid / 8);
   hipLaunchKernelGGL((k_gemm_tiled<F32, BM>), dim3((unsigned)grid), dim3(512), lds_bytes, s, g);
   return hipGetLastError();
 }
@@ -918,6 +948,7 @@ hipError_t launch_ws(gemm_group& g, hipStream_t s) {
       persistent_grid(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM, NG>), 64 * wsk::WAVES, lds_bytes, resident, total);
   if (grid < 0) return hipErrorInvalidDevice;
   g.total = (int32_t)total;
+  group_width(g, BM, BN, grid / 8);
   hipLaunchKernelGGL((k_gemm_ws<F32, BM, NG>), dim3((unsigned)grid), dim3(64 * wsk::WAVES), lds_bytes, s, g);
   return hipGetLastError();
 }

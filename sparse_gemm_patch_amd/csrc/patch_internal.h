@@ -66,6 +66,8 @@ struct gemm_problem {
   int32_t tn, tk;
   int32_t block0;  // first workgroup of this product in the launch
   int32_t blocks;  // its workgroups (the launch may pad after them)
+  float w_bytes;   // packed bytes per weight element (2 dense, 1.125 for 2:4, mean over tiles)
+  int32_t group_n; // tiled kernels: block columns per group of the block order
 };
 struct gemm_group {
   int32_t count;
