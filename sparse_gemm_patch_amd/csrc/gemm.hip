@@ -192,8 +192,9 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
 }
 
 // ------------------------------------------------------------------------
-// Tiled kernel for prefill-sized M (256 and 64 X rows per block; 128-row
-// blocks run on k_gemm_ws below).
+// Tiled kernel for prefill-sized M: 256 X rows per block, and 64 when two
+// workgroups share each CU (other 128- and 64-row blocks run on k_gemm_ws
+// below).
 //
 // Workgroup = 8 waves in a 2 x 4 grid; the block of Y^T is 256 W rows (n) x
 // BM X rows (m).  Wave (wn, wm) owns W rows 128 wn .. +127 (8 row blocks of
@@ -228,9 +229,9 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
 // never stall on the fill path.  The copies are issued from inline assembly
 // (which saves and restores M0, the LDS address register): the compiler
 // cannot tell that they target the other stage, and as builtins every LDS read
-// after them would wait for them to land.  The kernel issues no other
-// vector-memory loads, so the explicit waits are the only ones these copies
-// need.
+// after them would wait for them to land.  Its only other vector-memory loads
+// are the descriptor windows, waited for where they are loaded, so the
+// explicit waits are the only ones these copies need.
 // ------------------------------------------------------------------------
 namespace tiled {
 constexpr int BN = 256, BK = 64;
@@ -851,6 +852,21 @@ hipError_t launch_stream_group(gemm_group& g, int out_f32, hipStream_t s) {
 }
 
 namespace {
+// Opts `kernel` into lds_bytes of dynamic LDS (above the 64 KiB default),
+// once per device (done[device]).
+hipError_t allow_lds(const void* kernel, int lds_bytes, bool* done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!done[dev]) {
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    done[dev] = true;
+  }
+  return hipSuccess;
+}
+
 // Grid of a persistent launch: the workgroups the device holds at once
 // (queried once per device into cache[device]), rounded down to a multiple of
 // 8, and never more than the launch's slots.  -1 if the device cannot be
@@ -898,16 +914,12 @@ void group_width(gemm_group& g, int bm, int bn, int per_xcd) {
 
 template <bool F32, int BM>
 hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
-  constexpr int lds_bytes = tiled::STAGES * tiled::stage_bytes<BM>();  // above 64 KiB: opt in, once
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_tiled<F32, BM>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  constexpr int lds_bytes = tiled::STAGES * tiled::stage_bytes<BM>();
+  static bool lds_allowed[64] = {};
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(&k_gemm_tiled<F32, BM>), lds_bytes, lds_allowed);
+  if (e != hipSuccess) return e;
   // Each product's workgroups start at a multiple of 8 (the XCD count), so the
-  // block order inside it stays XCD-aware; the padding workgroups exit at once.
+  // block order inside it stays XCD-aware; padding slots are skipped.
   int64_t total = 0;
   for (int i = 0; i < g.count; ++i) {
     g.p[i].block0 = (int32_t)total;
@@ -929,13 +941,9 @@ hipError_t launch_ws(gemm_group& g, hipStream_t s) {
   constexpr int BN = 64 * NG;
   constexpr int lds_bytes = wsk::STAGES * wsk::stage_bytes<BM, NG>();  // 144 KiB at 128 x 256, 120 at 64 x 256
   static_assert(lds_bytes <= 160 * 1024, "LDS of one workgroup");
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM, NG>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool lds_allowed[64] = {};
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM, NG>), lds_bytes, lds_allowed);
+  if (e != hipSuccess) return e;
   int64_t total = 0;
   for (int i = 0; i < g.count; ++i) {
     g.p[i].block0 = (int32_t)total;
