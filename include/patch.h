@@ -140,7 +140,7 @@ patch_status patch_gemm(const patch_weight* w, const uint16_t* x, int64_t m, int
 
 /* patch_gemm with the kernel chosen by the caller, for tests and measurements.
  * `variant` <= 0 lets the library choose; for PATCH_KERNEL_TILED a positive
- * value forces the X rows per workgroup, 256, 128 or 64 (other values:
+ * value forces the X rows per workgroup, 256, 192, 128 or 64 (other values:
  * PATCH_E_INVALID_ARG).  It is ignored by PATCH_KERNEL_STREAM and
  * PATCH_KERNEL_AUTO.  PATCH_KERNEL_STREAM needs m <= 16. */
 patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx,

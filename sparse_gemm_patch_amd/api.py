@@ -155,7 +155,7 @@ class PackedWeight:
              kernel: str = "auto", block_m: int = 0, stream=None) -> torch.Tensor:
         """Y = X . W_masked^T for X bf16 [m][k]; returns Y [m][n] (bf16 or fp32).
 
-        kernel "tiled" takes block_m (X rows per workgroup: 256, 128 or 64; 0 =
+        kernel "tiled" takes block_m (X rows per workgroup: 256, 192, 128 or 64; 0 =
         the library's choice)."""
         m, ldx, out, ldy = self._operands(x, out, out_dtype)
         st = load().patch_gemm_kernel(self._h, ctypes.c_void_p(x.data_ptr()), m, ldx, ctypes.c_void_p(out.data_ptr()),

@@ -273,8 +273,8 @@ static patch_status gemm_group_common(const patch_gemm_item* items, int32_t coun
     return fail(PATCH_E_INVALID_ARG, "bad output dtype %d", (int)y_dtype);
   if (kernel != PATCH_KERNEL_AUTO && kernel != PATCH_KERNEL_TILED && kernel != PATCH_KERNEL_STREAM)
     return fail(PATCH_E_INVALID_ARG, "bad kernel %d", (int)kernel);
-  if (kernel == PATCH_KERNEL_TILED && variant > 0 && variant != 256 && variant != 128 && variant != 64)
-    return fail(PATCH_E_INVALID_ARG, "tiled block rows must be 256, 128 or 64, got %d", (int)variant);
+  if (kernel == PATCH_KERNEL_TILED && variant > 0 && variant != 256 && variant != 192 && variant != 128 && variant != 64)
+    return fail(PATCH_E_INVALID_ARG, "tiled block rows must be 256, 192, 128 or 64, got %d", (int)variant);
   if (count == 0) return ok();
   bool skip[PATCH_MAX_GROUP];
   for (int i = 0; i < count; ++i) {

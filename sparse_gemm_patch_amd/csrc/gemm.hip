@@ -192,9 +192,11 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
 }
 
 // ------------------------------------------------------------------------
-// Tiled kernel for prefill-sized M: 256 X rows per block, and 64 when two
-// workgroups share each CU (other 128- and 64-row blocks run on k_gemm_ws
-// below).
+// Tiled kernel for prefill-sized M: 256 or 192 X rows per block, and 64 when
+// two workgroups share each CU (other 128- and 64-row blocks run on k_gemm_ws
+// below).  192-row blocks fill the chip where 256-row ones leave many CUs
+// idle and 128-row ones leave a ragged second round (5120-wide products at
+// M = 2048: 220 against 160 or 320 workgroups, 11% faster).
 //
 // Workgroup = 8 waves in a 2 x 4 grid; the block of Y^T is 256 W rows (n) x
 // BM X rows (m).  Wave (wn, wm) owns W rows 128 wn .. +127 (8 row blocks of
@@ -972,7 +974,8 @@ int64_t padded_blocks(const gemm_group& g, int bm, int bn) {
 // (smaller blocks move more LDS bytes per flop), times the K steps.
 double block_cost(int bm, int64_t k) {
   // measured in whole rounds on the 8192x2048 and 4096x4096 products at M = 4096
-  const double eff = bm == 256 ? 1.0 : bm == 128 ? 0.96 : 0.68;
+  // (192: from the 8192x2048, 4096x4096 and 5120x5120 products, 0.84-0.96)
+  const double eff = bm == 256 ? 1.0 : bm == 192 ? 0.92 : bm == 128 ? 0.96 : 0.68;
   return bm / 256.0 / eff * (double)(k / 64);
 }
 }  // namespace
@@ -981,12 +984,12 @@ int tiled_block_m(const gemm_group& g) {
   // Estimated time of each block height: rounds of 256 workgroups when every
   // product has the same K, else total cost spread over the CUs but never less
   // than the longest workgroup.
-  const int bms[3] = {256, 128, 64};
+  const int bms[4] = {256, 192, 128, 64};
   bool same_k = true;
   for (int i = 1; i < g.count; ++i) same_k = same_k && g.p[i].k == g.p[0].k;
   int best = 256;
   double best_t = 0;
-  for (int j = 0; j < 3; ++j) {
+  for (int j = 0; j < 4; ++j) {
     int64_t blocks = 0;
     double cost = 0, longest = 0;
     for (int i = 0; i < g.count; ++i) {
@@ -1027,6 +1030,8 @@ hipError_t launch_tiled_group(gemm_group& g, int out_f32, int block_m, hipStream
       return out_f32 ? launch_tiled_bm<true, 64>(g, s) : launch_tiled_bm<false, 64>(g, s);
     case 128:
       return out_f32 ? launch_ws<true, 128, 4>(g, s) : launch_ws<false, 128, 4>(g, s);
+    case 192:
+      return out_f32 ? launch_tiled_bm<true, 192>(g, s) : launch_tiled_bm<false, 192>(g, s);
     default:
       return out_f32 ? launch_tiled_bm<true, 256>(g, s) : launch_tiled_bm<false, 256>(g, s);
   }

@@ -77,7 +77,7 @@ struct gemm_group {
 // The product of handle w with X [m][ldx] into Y [m][ldy] (block fields unset).
 gemm_problem make_problem(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y, int64_t ldy);
 // One launch of the streaming kernel (every m <= 16) / the tiled kernel over a
-// group.  block_m > 0 forces the tiled block height (256, 128, 64).
+// group.  block_m > 0 forces the tiled block height (256, 192, 128, 64).
 hipError_t launch_stream_group(gemm_group& g, int out_f32, hipStream_t s);
 hipError_t launch_tiled_group(gemm_group& g, int out_f32, int block_m, hipStream_t s);
 // The tiled block height the launcher would pick for a group.

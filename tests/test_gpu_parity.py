@@ -236,7 +236,7 @@ def test_stream_k_ranges_and_determinism(P, k, m):
     assert O.rel_error(y_host(y1), ref) <= 1e-4
 
 
-@pytest.mark.parametrize("block_m", [256, 128, 64])
+@pytest.mark.parametrize("block_m", [256, 192, 128, 64])
 @pytest.mark.parametrize("tn,tk,frac", [(128, 128, 0.5), (64, 64, 0.9), (128, 64, 0.0), (64, 128, 1.0)])
 def test_tiled_block_rows(P, block_m, tn, tk, frac):
     """Every block height of the tiled kernel: ragged M (300 rows) and N (640 = 2.5 blocks of 256)."""
@@ -260,9 +260,9 @@ def test_tiled_more_than_64_tile_columns(P, tn, tk, k):
     prob = I.make_problem("win", 300, 256, k, tn, tk, frac=0.5, cfg=52)
     pw = pack_problem(P, prob)
     x = dev_u16(prob.x)
-    ys = [pw.gemm(x, out_dtype=torch.float32, kernel="tiled", block_m=b) for b in (256, 128, 64)]
+    ys = [pw.gemm(x, out_dtype=torch.float32, kernel="tiled", block_m=b) for b in (256, 192, 128, 64)]
     torch.cuda.synchronize()
-    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+    assert all(torch.equal(ys[0], y) for y in ys[1:])
     ref = O.gemm_ref(prob.x, O.masked_weight(prob.w, prob.mask))
     assert O.rel_error(y_host(ys[0]), ref) <= 1e-4
 
@@ -287,7 +287,7 @@ def test_tiled_64_rows_every_kernel(P, m, n):
     assert O.rel_error(y_host(y32)[rows], ref) <= 1e-4
 
 
-@pytest.mark.parametrize("block_m", [256, 128, 64])
+@pytest.mark.parametrize("block_m", [256, 192, 128, 64])
 def test_tiled_block_rows_one_hot_exact(P, block_m):
     prob = I.make_problem("bmoh", 200, 256, 512, 64, 128, frac=0.7, cfg=49)
     ks = (np.arange(200) * 37 + 11) % 512
