@@ -5,6 +5,8 @@ Each case checks the packed format bit for bit against the oracle, Y against the
 fp64 oracle (all rows up to 300, 64 sampled rows above), bf16 Y against fp32 Y
 rounded to nearest even, and, for prefill-sized M, bitwise equality of Y across
 block heights (every kernel accumulates K in the same order)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -15,7 +17,7 @@ from sparse_gemm_patch_amd import inputs as I
 pytestmark = pytest.mark.gpu
 
 TILES = [(128, 128), (128, 64), (64, 128), (64, 64)]
-CASES = 32
+CASES = int(os.environ.get("PATCH_RANDOM_CASES", "32"))  # more for a longer sweep
 
 
 @pytest.fixture(scope="module")
