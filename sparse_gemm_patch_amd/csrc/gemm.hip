@@ -577,31 +577,36 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
 // ------------------------------------------------------------------------
 namespace wsk {
 constexpr int STAGES = 3, WAVES = 12;
-template <int BM, int NG> constexpr int stage_bytes() { return BM * 128 + NG * tiled::G_BYTES; }
+template <int BM, int NG> constexpr int step_bytes() { return BM * 128 + NG * tiled::G_BYTES; }
 }  // namespace wsk
 
 // Wait until at most n of this wave's copies are outstanding, and for its LDS
-// reads.  n is the copy count of one step: XC (2 or 4) X copies plus 0, 6 or 8
-// W copies.
+// reads.  n is the copy count of one stage: per K step XC (2 or 4) X copies
+// plus 0, 6 or 8 W copies, one or two K steps, so an even number up to 24.
 __device__ __forceinline__ void wait_copies_but(int n) {
 #define PATCH_WAIT_CASE(c) \
   case c: asm volatile("s_waitcnt vmcnt(" #c ") lgkmcnt(0)" ::: "memory"); break;
   switch (n) {
-    PATCH_WAIT_CASE(12) PATCH_WAIT_CASE(10) PATCH_WAIT_CASE(8) PATCH_WAIT_CASE(4) PATCH_WAIT_CASE(2)
+    PATCH_WAIT_CASE(24) PATCH_WAIT_CASE(22) PATCH_WAIT_CASE(20) PATCH_WAIT_CASE(18) PATCH_WAIT_CASE(16)
+    PATCH_WAIT_CASE(14) PATCH_WAIT_CASE(12) PATCH_WAIT_CASE(10) PATCH_WAIT_CASE(8) PATCH_WAIT_CASE(6)
+    PATCH_WAIT_CASE(4) PATCH_WAIT_CASE(2)
     default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
   }
 #undef PATCH_WAIT_CASE
 }
 
 // One output block of k_gemm_ws: workgroup slot `slot` of the launch; the
-// block is NG 64-row W groups (BN = 64 NG rows of W) by BM rows of X.
-template <bool F32, int BM, int NG>
+// block is NG 64-row W groups (BN = 64 NG rows of W) by BM rows of X.  A stage
+// holds KS consecutive 64-wide K steps (one barrier per stage): two halve the
+// barriers of the small 64 x 128 blocks, whose steps carry little work.
+template <bool F32, int BM, int NG, int KS>
 __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
   using namespace wsk;
   using tiled::G_BYTES;
   static_assert(NG == 2 || NG == 4, "128 or 256 W rows per block");
+  static_assert(KS == 1 || KS == 2, "one or two K steps per stage");
   constexpr int BN = 64 * NG, GW = NG / 2;  // GW: W groups per computing wave
-  constexpr int X_BYTES = BM * 128, STAGE_BYTES = stage_bytes<BM, NG>();
+  constexpr int X_BYTES = BM * 128, STEP_BYTES = step_bytes<BM, NG>(), STAGE_BYTES = KS * STEP_BYTES;
   constexpr int RW = BM / 4;   // X rows per copy wave and per compute wave
   constexpr int XC = RW / 8;   // X copies per copy wave
   constexpr int XB = RW / 16;  // X blocks of 16 rows per compute wave
@@ -623,6 +628,7 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
   int64_t n0, m0;
   block_origin<BM, BN>(n, m, local, P.group_n, n0, m0);
   const int nsteps = (int)(k / 64);
+  const int nstages = (nsteps + KS - 1) / KS;  // stage loads, KS K steps each (the last may hold fewer)
   const int ks = tk == 128;
   const int ns = tn == 128 ? 7 : 6;
   const int bt = tn >> 4;
@@ -648,8 +654,8 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
     const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(P.sparse_vals);
     const uint8_t* msrc = P.sparse_meta;
     const uint32_t loff16 = lane * 16, loff4 = lane * 4;
-    auto issue = [&](int step, int stage) -> int {
-      const uint32_t st = lds_base + stage * STAGE_BYTES;
+    // copies of K step `step` into the LDS bytes at st
+    auto issue_step = [&](int step, uint32_t st) -> int {
 #pragma unroll
       for (int j = 0; j < XC; ++j) dma16(xblk + step * 128, xoff[j], st + (RW * cw + 8 * j) * 128);
       const uint32_t gl = st + X_BYTES + cw * G_BYTES;
@@ -671,18 +677,26 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
       dma4(mp + 256, loff4, gl + 4096 + 256);
       return XC + 6;
     };
-    // Two steps ahead.  Before the barrier of step i this wave waits only for
-    // its copies of step i (those of step i + 1 were issued after them; vmcnt
-    // counts in issue order).  After it, every wave is done with step i - 1,
-    // whose stage takes step i + 2.
+    // copies of stage load t (K steps KS t ..) into LDS stage `stage`
+    auto issue = [&](int t, int stage) -> int {
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        if (KS * t + j < nsteps) c += issue_step(KS * t + j, lds_base + stage * STAGE_BYTES + j * STEP_BYTES);
+      return c;
+    };
+    // Two stage loads ahead.  Before the barrier of load i this wave waits only
+    // for its copies of load i (those of load i + 1 were issued after them;
+    // vmcnt counts in issue order).  After it, every wave is done with load
+    // i - 1, whose stage takes load i + 2.
     int pending = 0;
-    if (nsteps > 0) issue(0, 0);
-    if (nsteps > 1) pending = issue(1, 1);
+    if (nstages > 0) issue(0, 0);
+    if (nstages > 1) pending = issue(1, 1);
     int stage = 0;
-    for (int i = 0; i < nsteps; ++i) {
-      wait_copies_but(i + 1 < nsteps ? pending : 0);
+    for (int i = 0; i < nstages; ++i) {
+      wait_copies_but(i + 1 < nstages ? pending : 0);
       barrier();
-      if (i + 2 < nsteps) pending = issue(i + 2, stage == 0 ? 2 : stage - 1);
+      if (i + 2 < nstages) pending = issue(i + 2, stage == 0 ? 2 : stage - 1);
       stage = stage == 2 ? 0 : stage + 1;
     }
     return;
@@ -709,8 +723,9 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
   bf16x16 b[XB];
   bf16x8 a0[4 * GW], a1[4 * GW];
   int ix[4 * GW];
+  // operands of K step `step`, held in LDS stage `stage` at position step % KS
   auto load_ops = [&](int step, int stage) {
-    const uint8_t* cur = lds + stage * STAGE_BYTES;
+    const uint8_t* cur = lds + stage * STAGE_BYTES + (step % KS) * STEP_BYTES;
 #pragma unroll
     for (int h = 0; h < GW; ++h)
       dg[h] = hok[h] ? ((tile_desc[hdesc[h] + (step >> ks)] & 1) == PATCH_TILE_DENSE) : -1;
@@ -766,42 +781,49 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
   // i - 1 (read in the previous step) and then read step i, so that one of
   // them reads LDS while the other keeps the matrix unit busy.  Separate
   // loops keep the compiler from holding both schedules' registers.
+  // With KS = 2 the lagging waves multiply all but the last K step of a stage
+  // load at once and carry that one over the barrier.
   int stage = 0;
   if (wn == 0) {
-    for (int i = 0; i < nsteps; ++i) {
-      wait_copies_but(0);  // this wave's LDS reads of the previous step are done
-      barrier();           // step i is in `stage`
-      load_ops(i, stage);
-      mma();
+    for (int i = 0; i < nstages; ++i) {
+      wait_copies_but(0);  // this wave's LDS reads of the previous load are done
+      barrier();           // load i is in `stage`
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        if (KS * i + j < nsteps) {
+          load_ops(KS * i + j, stage);
+          mma();
+        }
       stage = stage == 2 ? 0 : stage + 1;
     }
   } else if (nsteps > 0) {
-    wait_copies_but(0);
-    barrier();
-    load_ops(0, 0);
-    stage = 1;
-    for (int i = 1; i < nsteps; ++i) {
+    for (int i = 0; i < nstages; ++i) {
       wait_copies_but(0);
       barrier();
-      mma();
-      load_ops(i, stage);
+      if (i > 0) mma();  // the last K step of load i - 1
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        if (KS * i + j < nsteps) {
+          if (j > 0) mma();
+          load_ops(KS * i + j, stage);
+        }
       stage = stage == 2 ? 0 : stage + 1;
     }
     mma();
   }
-  // After the last barrier only the stage of step nsteps - 1 is still read, and
-  // no copy is in flight: the stage step nsteps would have used holds the
-  // computing waves' Y blocks (8 x RW x 128 bytes).
+  // After the last barrier only the stage of load nstages - 1 is still read,
+  // and no copy is in flight: the stage load nstages would have used holds
+  // the computing waves' Y blocks (8 x RW x 128 bytes).
   static_assert(8 * RW * 128 <= STAGE_BYTES, "Y staging fits one stage");
-  uint8_t* region = lds + (nsteps % STAGES) * STAGE_BYTES + wave * (RW * 128);
+  uint8_t* region = lds + (nstages % STAGES) * STAGE_BYTES + wave * (RW * 128);
   store_block<F32, RW, XB, GW>(acc, region, P.y, P.ldy, m, m0 + RW * wm, wrow0, hok, lane);
 }
 
 // Persistent like k_gemm_tiled.
-template <bool F32, int BM, int NG>
+template <bool F32, int BM, int NG, int KS>
 __global__ __launch_bounds__(768, 1) void k_gemm_ws(const gemm_group g) {
   for (int slot = blockIdx.x; slot < g.total; slot += gridDim.x) {
-    ws_block<F32, BM, NG>(g, slot);
+    ws_block<F32, BM, NG, KS>(g, slot);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
@@ -938,13 +960,13 @@ hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool F32, int BM, int NG>
+template <bool F32, int BM, int NG, int KS>
 hipError_t launch_ws(gemm_group& g, hipStream_t s) {
   constexpr int BN = 64 * NG;
-  constexpr int lds_bytes = wsk::STAGES * wsk::stage_bytes<BM, NG>();  // 144 KiB at 128 x 256, 120 at 64 x 256
+  constexpr int lds_bytes = wsk::STAGES * KS * wsk::step_bytes<BM, NG>();  // 144 KiB at 128 x 256
   static_assert(lds_bytes <= 160 * 1024, "LDS of one workgroup");
   static bool lds_allowed[64] = {};
-  const hipError_t e = allow_lds(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM, NG>), lds_bytes, lds_allowed);
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM, NG, KS>), lds_bytes, lds_allowed);
   if (e != hipSuccess) return e;
   int64_t total = 0;
   for (int i = 0; i < g.count; ++i) {
@@ -955,11 +977,11 @@ hipError_t launch_ws(gemm_group& g, hipStream_t s) {
   if (total == 0) return hipSuccess;
   static int resident[64] = {};
   const int grid =
-      persistent_grid(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM, NG>), 64 * wsk::WAVES, lds_bytes, resident, total);
+      persistent_grid(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM, NG, KS>), 64 * wsk::WAVES, lds_bytes, resident, total);
   if (grid < 0) return hipErrorInvalidDevice;
   g.total = (int32_t)total;
   group_width(g, BM, BN, grid / 8);
-  hipLaunchKernelGGL((k_gemm_ws<F32, BM, NG>), dim3((unsigned)grid), dim3(64 * wsk::WAVES), lds_bytes, s, g);
+  hipLaunchKernelGGL((k_gemm_ws<F32, BM, NG, KS>), dim3((unsigned)grid), dim3(64 * wsk::WAVES), lds_bytes, s, g);
   return hipGetLastError();
 }
 
@@ -1024,12 +1046,12 @@ hipError_t launch_tiled_group(gemm_group& g, int out_f32, int block_m, hipStream
       // and when it would leave half the CUs idle, blocks of 128 W rows
       // (twice the workgroups) are faster still.
       if (padded_blocks(g, 64, 256) <= 128)
-        return out_f32 ? launch_ws<true, 64, 2>(g, s) : launch_ws<false, 64, 2>(g, s);
+        return out_f32 ? launch_ws<true, 64, 2, 2>(g, s) : launch_ws<false, 64, 2, 2>(g, s);
       if (padded_blocks(g, 64, 256) <= 256)
-        return out_f32 ? launch_ws<true, 64, 4>(g, s) : launch_ws<false, 64, 4>(g, s);
+        return out_f32 ? launch_ws<true, 64, 4, 1>(g, s) : launch_ws<false, 64, 4, 1>(g, s);
       return out_f32 ? launch_tiled_bm<true, 64>(g, s) : launch_tiled_bm<false, 64>(g, s);
     case 128:
-      return out_f32 ? launch_ws<true, 128, 4>(g, s) : launch_ws<false, 128, 4>(g, s);
+      return out_f32 ? launch_ws<true, 128, 4, 1>(g, s) : launch_ws<false, 128, 4, 1>(g, s);
     case 192:
       return out_f32 ? launch_tiled_bm<true, 192>(g, s) : launch_tiled_bm<false, 192>(g, s);
     default:
