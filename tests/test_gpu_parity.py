@@ -221,7 +221,7 @@ def test_ones_count_kept_exactly(P, kernel, m):
     assert np.array_equal(y_host(y), np.broadcast_to(want, (m, 256)))
 
 
-@pytest.mark.parametrize("k", [64, 192, 1088, 2048])
+@pytest.mark.parametrize("k", [64, 192, 1088, 2048, 4160])
 @pytest.mark.parametrize("m", [1, 5, 16])
 def test_stream_k_ranges_and_determinism(P, k, m):
     """16 waves share the K chunks of a block: fewer chunks than waves, a ragged last round, many rounds."""
