@@ -57,6 +57,21 @@ __device__ __forceinline__ void store4(void* y, int64_t ldy, int64_t m, int64_t 
   }
 }
 
+// global -> LDS copy of 16 (or 4) bytes per lane from base + off (base
+// wave-uniform, off a 32-bit per-lane byte offset); lane i writes LDS bytes
+// lds_addr + 16 i (4 i).  lds_addr must be wave-uniform.  A scalar base keeps
+// one VGPR per copy stream instead of a 64-bit address.
+__device__ __forceinline__ bf16x8 lds8(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(off), "s"(base) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(off), "s"(base) : "memory");
+}
 // ------------------------------------------------------------------------
 // Streaming kernel for M <= 16 (decode).
 //
@@ -120,8 +135,20 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
   const int blk = (int)((n0 & (tn - 1)) >> 4);   // this block's 16-row block inside its tile
   const int bt = tn >> 4;
 
-  const bool m_ok = r16 < m;
-  const uint16_t* xrow = x + (int64_t)(m_ok ? r16 : 0) * ldx + 8 * q;
+  // X goes through LDS: per chunk two copies of 8 rows x 128 bytes (whole
+  // lines), 16-byte chunk c of row r at position c ^ (r & 7), into this wave's
+  // slot of the batch; rows past M repeat row M - 1 (they only feed Y rows that
+  // are never stored).  Read straight into the B operand, every load touched
+  // 16 rows x 64 bytes.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[WAVES * BATCH * 2048];
+  const uint32_t slot0 = (uint32_t)(uintptr_t)smem + (uint32_t)(wave * BATCH * 2048);
+  uint32_t xoff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * h + (lane >> 3);
+    const int64_t rc = row < m ? row : m - 1;
+    xoff[h] = (uint32_t)((rc * ldx + 8 * ((lane & 7) ^ (row & 7))) * 2);
+  }
   const uint8_t* dbase = reinterpret_cast<const uint8_t*>(dense_vals) + lane * 16;
   const uint8_t* sbase = reinterpret_cast<const uint8_t*>(sparse_vals) + lane * 16;
   const uint8_t* mbase = sparse_meta + lane * 8;
@@ -147,7 +174,9 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
 #pragma unroll
       for (int t = 0; t < BATCH; ++t) {
         const int64_t c = base + (int64_t)WAVES * min(j + t, nj - 1);
-        xb[t] = m_ok ? cat16(ld8(xrow + (c << 6)), ld8(xrow + (c << 6) + 32)) : cat16(zero8(), zero8());
+        const uint16_t* xc = x + (c << 6);
+        dma16(xc, xoff[0], slot0 + t * 2048);
+        dma16(xc, xoff[1], slot0 + t * 2048 + 1024);
         const int64_t slot = d[t] >> 1;
         const int64_t u = (c & ks) * bt + blk;  // operand unit of this block and chunk
         const bool dn = (d[t] & 1) == PATCH_TILE_DENSE;
@@ -156,6 +185,13 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
         const uint8_t* cw = mbase + slot * tn * (tk >> 3) + (u >> 2) * 512;  // lane's 8 bytes of codes
         a0[t] = *reinterpret_cast<const bf16x8*>(dn ? dw : sw);
         w2[t] = *reinterpret_cast<const u32x4*>(dn ? dw + 1024 : cw);  // dense positions (2,3), or the codes
+      }
+      // the X copies are not loads the compiler knows of: wait for them here
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int t = 0; t < BATCH; ++t) {
+        const uint8_t* sl = smem + (wave * BATCH + t) * 2048 + r16 * 128;
+        xb[t] = cat16(lds8(sl + ((q ^ (r16 & 7)) << 4)), lds8(sl + (((4 + q) ^ (r16 & 7)) << 4)));
       }
 #pragma unroll
       for (int t = 0; t < BATCH; ++t) {
@@ -175,7 +211,10 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
   }
 
   // Sum the waves in a fixed order: lane holds rows 4 q + i of column m = r16.
-  __shared__ float red[WAVES][16][17];
+  // The X slots are free once every wave is past its last chunk.
+  static_assert(WAVES * 16 * 17 * 4 <= WAVES * BATCH * 2048, "reduction fits the X slots");
+  float(*red)[16][17] = reinterpret_cast<float(*)[16][17]>(smem);
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][4 * q + i][r16] = acc[i];
   __syncthreads();
@@ -243,26 +282,11 @@ template <int BM> constexpr int x_bytes() { return BM * 128; }
 template <int BM> constexpr int stage_bytes() { return x_bytes<BM>() + 4 * G_BYTES; }
 }  // namespace tiled
 
-// global -> LDS copy of 16 (or 4) bytes per lane from base + off (base
-// wave-uniform, off a 32-bit per-lane byte offset); lane i writes LDS bytes
-// lds_addr + 16 i (4 i).  lds_addr must be wave-uniform.  A scalar base keeps
-// one VGPR per copy stream instead of a 64-bit address.
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(lds_addr), "v"(off), "s"(base) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(lds_addr), "v"(off), "s"(base) : "memory");
-}
 // Wait for this wave's copies and LDS reads, then synchronise the workgroup.
 __device__ __forceinline__ void step_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
-__device__ __forceinline__ bf16x8 lds8(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ int xswz(int r) { return r & 7; }
 
 // Output block of this workgroup.  The dispatcher deals workgroup i to XCD
