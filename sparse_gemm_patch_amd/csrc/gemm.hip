@@ -183,8 +183,9 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
         const uint8_t* dw = dbase + (slot * tn * tk + u * 1024) * 2;
         const uint8_t* sw = sbase + slot * tn * tk + u * 1024;
         const uint8_t* cw = mbase + slot * tn * (tk >> 3) + (u >> 2) * 512;  // lane's 8 bytes of codes
-        a0[t] = *reinterpret_cast<const bf16x8*>(dn ? dw : sw);
-        w2[t] = *reinterpret_cast<const u32x4*>(dn ? dw + 1024 : cw);  // dense positions (2,3), or the codes
+        // W is read once: non-temporal loads keep it from displacing X in the caches
+        a0[t] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dn ? dw : sw)));
+        w2[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dn ? dw + 1024 : cw));  // dense (2,3), or codes
       }
       // the X copies are not loads the compiler knows of: wait for them here
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
