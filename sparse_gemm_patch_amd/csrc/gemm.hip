@@ -20,6 +20,9 @@
 // lane's A operand is one 16-byte load and a wave's is 1 KiB contiguous.
 #include "patch_internal.h"
 
+#include <atomic>
+#include <climits>
+
 namespace {
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
@@ -894,6 +897,7 @@ hipError_t launch_stream_group(gemm_group& g, int out_f32, hipStream_t s) {
     total += (g.p[i].blocks + 7) / 8 * 8;
   }
   if (total == 0) return hipSuccess;
+  if (total > INT32_MAX) return hipErrorInvalidValue;  // block numbers are 32-bit
   const dim3 block(64 * streamk::WAVES);
   if (out_f32) hipLaunchKernelGGL(k_gemm_stream<true>, dim3((unsigned)total), block, 0, s, g);
   else hipLaunchKernelGGL(k_gemm_stream<false>, dim3((unsigned)total), block, 0, s, g);
@@ -902,16 +906,17 @@ hipError_t launch_stream_group(gemm_group& g, int out_f32, hipStream_t s) {
 
 namespace {
 // Opts `kernel` into lds_bytes of dynamic LDS (above the 64 KiB default),
-// once per device (done[device]).
-hipError_t allow_lds(const void* kernel, int lds_bytes, bool* done) {
+// once per device (done[device]; host threads that race here set the same
+// attribute).
+hipError_t allow_lds(const void* kernel, int lds_bytes, std::atomic<bool>* done) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!done[dev]) {
+  if (!done[dev].load(std::memory_order_acquire)) {
     e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
-    done[dev] = true;
+    done[dev].store(true, std::memory_order_release);
   }
   return hipSuccess;
 }
@@ -920,18 +925,20 @@ hipError_t allow_lds(const void* kernel, int lds_bytes, bool* done) {
 // (queried once per device into cache[device]), rounded down to a multiple of
 // 8, and never more than the launch's slots.  -1 if the device cannot be
 // queried.
-int persistent_grid(const void* kernel, int threads, int lds_bytes, int* cache, int64_t slots) {
+int persistent_grid(const void* kernel, int threads, int lds_bytes, std::atomic<int>* cache, int64_t slots) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  if (cache[dev] == 0) {
+  int held = cache[dev].load(std::memory_order_relaxed);
+  if (held == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds_bytes) != hipSuccess)
       return -1;
     const int r = cus * (per_cu > 0 ? per_cu : 1) / 8 * 8;
-    cache[dev] = r > 8 ? r : 8;
+    held = r > 8 ? r : 8;
+    cache[dev].store(held, std::memory_order_relaxed);
   }
-  return slots < cache[dev] ? (int)slots : cache[dev];
+  return slots < held ? (int)slots : held;
 }
 
 // The workgroups resident on one XCD (per_xcd of them) take consecutive
@@ -964,7 +971,7 @@ void group_width(gemm_group& g, int bm, int bn, int per_xcd) {
 template <bool F32, int BM>
 hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
   constexpr int lds_bytes = tiled::STAGES * tiled::stage_bytes<BM>();
-  static bool lds_allowed[64] = {};
+  static std::atomic<bool> lds_allowed[64] = {};
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(&k_gemm_tiled<F32, BM>), lds_bytes, lds_allowed);
   if (e != hipSuccess) return e;
   // Each product's workgroups start at a multiple of 8 (the XCD count), so the
@@ -976,7 +983,8 @@ hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
     total += (g.p[i].blocks + 7) / 8 * 8;
   }
   if (total == 0) return hipSuccess;
-  static int resident[64] = {};
+  if (total > INT32_MAX) return hipErrorInvalidValue;  // block numbers are 32-bit
+  static std::atomic<int> resident[64] = {};
   const int grid = persistent_grid(reinterpret_cast<const void*>(&k_gemm_tiled<F32, BM>), 512, lds_bytes, resident, total);
   if (grid < 0) return hipErrorInvalidDevice;
   g.total = (int32_t)total;
@@ -990,7 +998,7 @@ hipError_t launch_ws(gemm_group& g, hipStream_t s) {
   constexpr int BN = 64 * NG;
   constexpr int lds_bytes = wsk::STAGES * KS * wsk::step_bytes<BM, NG>();  // 144 KiB at 128 x 256
   static_assert(lds_bytes <= 160 * 1024, "LDS of one workgroup");
-  static bool lds_allowed[64] = {};
+  static std::atomic<bool> lds_allowed[64] = {};
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM, NG, KS>), lds_bytes, lds_allowed);
   if (e != hipSuccess) return e;
   int64_t total = 0;
@@ -1000,7 +1008,8 @@ hipError_t launch_ws(gemm_group& g, hipStream_t s) {
     total += (g.p[i].blocks + 7) / 8 * 8;
   }
   if (total == 0) return hipSuccess;
-  static int resident[64] = {};
+  if (total > INT32_MAX) return hipErrorInvalidValue;  // block numbers are 32-bit
+  static std::atomic<int> resident[64] = {};
   const int grid =
       persistent_grid(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM, NG, KS>), 64 * wsk::WAVES, lds_bytes, resident, total);
   if (grid < 0) return hipErrorInvalidDevice;
