@@ -1,0 +1,63 @@
+"""bench.py end to end on the GPU: one JSON line with the fields the benchmark
+contract names, a roofline whose fraction is its achieved rate over its peak, and
+a CPU-oracle baseline that also checked the GPU output.  Runs the default
+(1B prefill) and the decode workload with few steps, each in a child process."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from conftest import ROOT
+
+pytestmark = pytest.mark.gpu
+
+TOP = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+       "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline")
+
+
+def run_bench(*extra):
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1", "--no-sweep",
+           "--no-grouped", "--no-sample", "--no-split", *extra]
+    print("bench:", " ".join(cmd[1:]), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.strip().splitlines() if ln.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    return json.loads(lines[0])
+
+
+def check_common(d, steps=3, warmup=1):
+    for key in TOP:
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == steps and d["warmup"] == warmup
+    assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
+    assert d["data"] == "synthetic" and d["dtype"] == "bf16" and d["vs_baseline"] is None
+    assert isinstance(d["config"], dict) and d["config"]["workload"]
+    r = d["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert key in r, key
+    assert r["achieved"] > 0 and r["peak"] > 0
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    return r
+
+
+def test_default_workload_line():
+    d = run_bench("--cpu-rows", "256")
+    r = check_common(d)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+    # value is the dense-equivalent rate of the step
+    assert abs(d["dense_equiv_frac_of_peak"] - d["value"] / 2500.0) < 1e-3
+    c = d["cpu_baseline"]
+    for key in ("value", "unit", "cores", "kind", "sample"):
+        assert key in c, key
+    assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1
+    assert c["parity_max_rel"] <= 1e-2
+
+
+def test_decode_workload_line():
+    d = run_bench("--workload", "llama7b-decode", "--no-cpu-baseline")
+    r = check_common(d)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert d["cpu_baseline"] is None and d["weight_copies"] >= 2
