@@ -22,7 +22,8 @@
  *     16-byte aligned.
  *   - bf16 values are passed as uint16_t bit patterns.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued on
- *     it in order; only patch_pack and patch_export block the host.
+ *     it in order; only patch_pack, patch_import and patch_export block the
+ *     host.
  *   - Every call returns a patch_status.  Nothing aborts and no C++ exception
  *     crosses the ABI.  On failure patch_last_error() returns a message (per
  *     thread, valid until the next call on that thread).
@@ -208,7 +209,8 @@ patch_status patch_get_info(const patch_weight* w, patch_info* info);
 
 /* Copy the packed arrays to host buffers (any may be NULL to skip).  Sizes are
  * tiles (u8 / i32 per tile) and the byte counts of patch_info.  Blocks the host
- * until the copies and all work queued on the handle's last stream are done. */
+ * until the copies are done.  The packed arrays never change after patch_pack or
+ * patch_import returns, so GEMMs on the handle may still be in flight. */
 patch_status patch_export(const patch_weight* w, uint8_t* tile_map, int32_t* tile_slot,
                           uint16_t* dense_vals, uint16_t* sparse_vals, uint8_t* sparse_meta);
 

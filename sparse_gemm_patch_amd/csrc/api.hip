@@ -151,7 +151,6 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
   pw->tiles_n = n / tile_n;
   pw->tiles_k = k / tile_k;
   pw->tiles = tiles;
-  pw->last_stream = s;
 
   if (tiles == 0) {
     if (info) fill_info(pw, info);
@@ -301,7 +300,6 @@ static patch_status gemm_group_common(const patch_gemm_item* items, int32_t coun
   for (int i = 0; i < count; ++i) {
     if (skip[i]) continue;
     const patch_gemm_item& it = items[i];
-    const_cast<patch_weight*>(it.w)->last_stream = s;
     if (it.w->k == 0) {
       e = launch_fill_zero_y(it.y, it.m, it.w->n, it.ldy, f32, s);
       if (e != hipSuccess) return hip_fail(e, "zero-fill launch");
@@ -356,7 +354,6 @@ patch_status patch_unpack(const patch_weight* w, uint16_t* w_out, int64_t ldw, v
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev != w->device) return fail(PATCH_E_INVALID_ARG, "weight lives on device %d, current device is %d", w->device, dev);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const_cast<patch_weight*>(w)->last_stream = s;
   e = launch_decompress(w, w_out, ldw, s);
   if (e != hipSuccess) return hip_fail(e, "unpack launch");
   return ok();
@@ -399,8 +396,9 @@ static patch_status export_impl(const patch_weight* w, uint8_t* tile_map, int32_
                                 uint16_t* sparse_vals, uint8_t* sparse_meta) {
   if (!w) return fail(PATCH_E_INVALID_ARG, "weight handle is NULL");
   if (w->tiles == 0) return ok();
-  hipError_t e = hipStreamSynchronize(w->last_stream);
-  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  // The pools never change once patch_pack / patch_import have returned (both
+  // block until they are complete), so no stream needs waiting for here.
+  hipError_t e = hipSuccess;
   if (tile_map) {
     e = hipMemcpy(tile_map, w->tile_map, (size_t)w->tiles, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy tile_map");
@@ -547,7 +545,6 @@ patch_status patch_import(int64_t n, int64_t k, int32_t tile_n, int32_t tile_k, 
   pw->tiles = tiles;
   pw->n_dense = nd;
   pw->n_sparse = ns;
-  pw->last_stream = s;
   if (tiles == 0) {
     if (info) fill_info(pw, info);
     *out = pw;

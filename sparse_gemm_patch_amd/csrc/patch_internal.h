@@ -23,7 +23,6 @@ struct patch_weight {
   uint16_t* dense_vals;  // [D][TN][TK]
   uint16_t* sparse_vals; // [S][TN][TK/2]
   uint8_t* sparse_meta;  // [S][TN][TK/8]
-  hipStream_t last_stream;
 };
 
 // Sentinel for "no invalid group found".
