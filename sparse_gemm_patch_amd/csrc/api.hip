@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <new>
 #include <string>
 #include <vector>
@@ -41,7 +42,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 hipError_t dev_alloc(void** p, size_t bytes) {
   *p = nullptr;
   if (bytes == 0) return hipSuccess;
-  static int counter = 0;
+  static std::atomic<int> counter{0};
   const char* env = getenv("PATCH_TEST_FAIL_ALLOC");
   if (env && *env) {
     const int nth = atoi(env);
@@ -62,8 +63,8 @@ patch_status check_device(int* dev_out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  static int cache[64];  // 0 unknown, 1 supported, 2 unsupported
-  if (dev >= 0 && dev < 64 && cache[dev] == 1) {
+  static std::atomic<int> cache[64];  // 0 unknown, 1 supported, 2 unsupported
+  if (dev >= 0 && dev < 64 && cache[dev].load(std::memory_order_relaxed) == 1) {
     *dev_out = dev;
     return PATCH_OK;
   }
@@ -71,7 +72,7 @@ patch_status check_device(int* dev_out) {
   e = hipGetDeviceProperties(&prop, dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
   const bool supported = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev >= 0 && dev < 64) cache[dev] = supported ? 1 : 2;
+  if (dev >= 0 && dev < 64) cache[dev].store(supported ? 1 : 2, std::memory_order_relaxed);
   if (!supported) return fail(PATCH_E_UNSUPPORTED, "device %d is %s; only gfx950 is supported", dev, prop.gcnArchName);
   *dev_out = dev;
   return PATCH_OK;
