@@ -44,6 +44,42 @@ def test_one_handle_on_two_streams(P):
             assert torch.equal(o, w)
 
 
+def test_one_handle_from_two_host_threads(P):
+    """Two host threads launch on one handle, each on its own stream (ctypes
+    drops the interpreter lock during the call, so the library runs in both at
+    once): every Y equals the single-threaded one bit for bit."""
+    import threading
+    prob = I.make_problem("th", 256, 512, 1024, 128, 128, frac=0.9, cfg=91)
+    pw = P.pack(dev_u16(prob.w), torch.from_numpy(prob.bits).cuda(), tile=(128, 128))
+    ms = (16, 256)  # the streaming and the tiled kernel
+    xs = {m: dev_u16(I.gen_x(m, 1024, I.rng_for(91, m, I.ROLE_X))) for m in ms}
+    want = {m: pw.gemm(xs[m]) for m in ms}
+    torch.cuda.synchronize()
+    outs = {(t, r): None for t in range(2) for r in range(20)}
+    errors = []
+
+    def worker(t):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for r in range(20):
+                    outs[(t, r)] = pw.gemm(xs[ms[(t + r) % 2]])
+            st.synchronize()
+        except Exception as e:  # reported below, on the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in threads), "a launching thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for (t, r), y in outs.items():
+        assert torch.equal(y, want[ms[(t + r) % 2]]), (t, r)
+
+
 def test_grouped_layer_in_a_graph(P):
     """q+k+v and o stages of a shrunk 1B layer captured once, replayed on new inputs."""
     names = list(I.LLAMA32_1B)
