@@ -84,13 +84,14 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t ld
 // Y^T, and are summed through LDS in a fixed order.  No workgroup depends on
 // another (a cross-workgroup reduction would need device-scope fences, which
 // write back a whole XCD's L2 on this chip).  Per chunk a wave loads its A
-// operand (1 KiB of 2:4 values or 2 KiB of dense positions, contiguous) and the
-// 16 X rows (two 16-byte loads per lane, rows past M read as zero), BATCH
-// chunks at a time.
+// operand (1 KiB of 2:4 values or 2 KiB of dense positions, contiguous, with
+// non-temporal loads) and copies the 16 X rows into its own LDS slot (two
+// global_load_lds copies of 8 rows x 128 bytes; rows past M repeat row M - 1),
+// BATCH chunks at a time.
 // ------------------------------------------------------------------------
 namespace streamk {
 constexpr int WAVES = 16;
-constexpr int BATCH = 2;  // chunks per wave whose loads are in flight together (1, 2, 4: within 5%; 8: 2x slower)
+constexpr int BATCH = 2;  // chunks per wave in flight together (1: 7-20% slower; 4: up to 19% slower, one workgroup per CU)
 }  // namespace streamk
 
 // The product a workgroup belongs to (a short scalar scan over the group) and
