@@ -199,18 +199,55 @@ patch_status patch_unpack(const patch_weight* w, uint16_t* w_out, int64_t ldw, v
  * patch_mask_unpack -- expand `count` packed mask bits into bytes 0/1
  * (out[i] = bit i in `order`).  Pad bits past `count` are ignored.
  *
- *   bits  device, ceil(count/8) bytes.   out  device, count bytes.
+ * The released artifact of the method is a binary keep/prune mask stored
+ * bit-packed in mask.npz (model card "llama_3.2_1b-PATCH-45Sparse",
+ * description; the MaskLLM card "gemma_3_1b-MaskLLM-50Sparse", description,
+ * ships its mask the same way).  The pages do not state the bit order; both
+ * orders are accepted, 1 = keep.
+ *
+ *   bits   device, at least ceil(count/8) bytes.  Read only.
+ *   count  number of mask bits, >= 0 (0 is a no-op).
+ *   out    device, at least count bytes, written.  May have any alignment.
+ *
+ * Errors: PATCH_E_INVALID_ARG for a bad order, count < 0 or a NULL pointer
+ * when count > 0; PATCH_E_UNSUPPORTED off gfx950.  Buffer sizes cannot be
+ * checked here: a short `bits` or `out` is read or written out of bounds.
+ * Never allocates, never blocks the host.
  */
 patch_status patch_mask_unpack(const uint8_t* bits, int64_t count, patch_bit_order order,
                                uint8_t* out, void* stream);
 
-/* Shape, tile counts, pool sizes and sparsity of a packed weight (host struct). */
+/*
+ * patch_get_info -- shape, tile counts, pool sizes and sparsity of a packed
+ * weight.  `sparsity` is the fraction of pruned weights, 0.5 * S / (D + S):
+ * the pages report the measured mask sparsity this way, 44.99% for a 45%
+ * target (model card "llama_3.2_1b-PATCH-45Sparse", description) and 50.00%
+ * when every tile is 2:4 (card "gemma_3_1b-MaskLLM-50Sparse", description).
+ *
+ *   w     handle.   info  host struct, written (bad_* are -1).
+ *
+ * Errors: PATCH_E_INVALID_ARG for a NULL argument.  No device work.
+ */
 patch_status patch_get_info(const patch_weight* w, patch_info* info);
 
-/* Copy the packed arrays to host buffers (any may be NULL to skip).  Sizes are
- * tiles (u8 / i32 per tile) and the byte counts of patch_info.  Blocks the host
- * until the copies are done.  The packed arrays never change after patch_pack or
- * patch_import returns, so GEMMs on the handle may still be in flight. */
+/*
+ * patch_export -- copy the packed arrays to host buffers in the format
+ * described under patch_pack.  The pages define the tile types (dense or 2:4,
+ * "PATCH: Learnable Tile-level Hybrid Sparsity for LLMs", Abstract) but give
+ * no storage format for a packed weight; the exported format is this
+ * library's own (kept values in ascending k, 4-bit codes, separate pools), and
+ * it is what the CPU oracle produces, so the two can be compared bit for bit.
+ *
+ *   tile_map, tile_slot   host, tiles = tiles_n * tiles_k entries (u8, i32).
+ *   dense_vals, sparse_vals, sparse_meta   host, bytes_dense,
+ *                         bytes_sparse_vals and bytes_sparse_meta bytes.
+ *   Any of them may be NULL to skip that array.
+ *
+ * Errors: PATCH_E_INVALID_ARG for a NULL handle, PATCH_E_HIP if a copy fails,
+ * PATCH_E_NOMEM if host staging memory runs out.  Blocks the host until the
+ * copies are done.  The packed arrays never change after patch_pack or
+ * patch_import returns, so GEMMs on the handle may still be in flight.
+ */
 patch_status patch_export(const patch_weight* w, uint8_t* tile_map, int32_t* tile_slot,
                           uint16_t* dense_vals, uint16_t* sparse_vals, uint8_t* sparse_meta);
 

@@ -170,6 +170,9 @@ class PackedWeight:
         """Masked dense W (bf16 [n][k]), pruned weights +0.0."""
         if out is None:
             out = torch.empty((self.n, self.k), dtype=torch.bfloat16, device=self.device)
+        # shape first: the kernel writes n rows of k values at out's row stride
+        if tuple(out.shape) != (self.n, self.k):
+            raise ValueError(f"out must be [{self.n}][{self.k}], got {list(out.shape)}")
         _check_cuda(out, "out", torch.bfloat16)
         ldw = _row_major_2d(out, "out") if out.numel() else self.k
         st = load().patch_unpack(self._h, ctypes.c_void_p(out.data_ptr()), ldw, _stream_handle(stream))
@@ -226,7 +229,14 @@ def import_packed(arrays: dict, n: int, k: int, tile=(128, 128), device=None, st
     """Rebuild a packed weight from the arrays PackedWeight.export returns (tile_slot is implied
     by tile_map and ignored).  The arrays are host numpy arrays; the weight lands on `device`."""
     tn, tk = int(tile[0]), int(tile[1])
+    n, k = int(n), int(k)
+    if tn not in (64, 128) or tk not in (64, 128) or n < 0 or k < 0 or n % tn or k % tk:
+        raise ValueError(f"W {n}x{k} is not a whole number of {tn}x{tk} tiles (each side 64 or 128)")
     tm = np.ascontiguousarray(arrays["tile_map"], dtype=np.uint8).reshape(-1)
+    # the library reads exactly (n/tn)*(k/tk) tile-map bytes and sizes the pools from them
+    if tm.size != (n // tn) * (k // tk):
+        raise ValueError(f"tile_map has {tm.size} entries, a {n}x{k} weight in {tn}x{tk} tiles has "
+                         f"{(n // tn) * (k // tk)}")
     nd = int(np.count_nonzero(tm == DENSE))
     ns = int(np.count_nonzero(tm == SPARSE24))
     want = {"dense_vals": (np.uint16, nd * tn * tk), "sparse_vals": (np.uint16, ns * tn * tk // 2),
@@ -308,6 +318,14 @@ def sample_mask(tile_logits: torch.Tensor, group_logits: torch.Tensor, n: int, k
 def mask_unpack(bits: torch.Tensor, count: int, bit_order: str = "big", out: Optional[torch.Tensor] = None,
                 stream=None) -> torch.Tensor:
     """Expand `count` packed mask bits to uint8 0/1 on the GPU."""
+    count = int(count)
+    if count < 0:
+        raise ValueError("count must be >= 0")
+    # sizes first: the kernel reads ceil(count/8) bytes of bits and writes count bytes of out
+    if bits.numel() * 8 < count or not bits.is_contiguous():
+        raise ValueError(f"bits must be contiguous and hold at least {count} bits, got {bits.numel()} bytes")
+    if out is not None and (out.numel() < count or not out.is_contiguous()):
+        raise ValueError(f"out must be contiguous with at least {count} elements, got {out.numel()}")
     _check_cuda(bits, "bits", torch.uint8)
     if out is None:
         out = torch.empty(count, dtype=torch.uint8, device=bits.device)

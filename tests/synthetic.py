@@ -1,8 +1,10 @@
 """Seeded synthetic inputs for the hybrid dense / 2:4 tile GEMM.
 
-This module is shared by the CPU oracle's tests, the GPU parity tests and the
-benchmark.  It draws random numbers and builds masks; it holds none of the
-packing or GEMM arithmetic that the library and the oracle implement.
+Test and measurement infrastructure: the CPU oracle's tests, the GPU parity
+tests, the smoke check and the benchmark draw their inputs from here; the
+library never imports it.  It draws random numbers and builds masks; it holds
+none of the packing or GEMM arithmetic that the library and the oracle
+implement.
 
 The workloads follow the PATCH pages:
   * weights are an ``nn.Linear`` weight ``W[N][K]`` (out x in), loaded in bf16
@@ -82,23 +84,34 @@ def choose_sparse_tiles(tiles: int, n_sparse: int, rng: np.random.Generator) -> 
     return sel
 
 
+def magnitude_top2(w_bits: np.ndarray) -> np.ndarray:
+    """u8[N][K]: 1 where a weight is one of the two largest |w| of its aligned group of four
+    along K (on equal magnitudes the lower index wins)."""
+    n, k = w_bits.shape
+    mag = np.abs(bf16_bits_to_f32(w_bits)).reshape(n, k // 4, 4)
+    # stable argsort on -|w| keeps the lower index first among equal magnitudes
+    order = np.argsort(-mag, axis=2, kind="stable")
+    top2 = np.zeros_like(mag, dtype=np.uint8)
+    np.put_along_axis(top2, order[:, :, :2], 1, axis=2)
+    return top2.reshape(n, k)
+
+
+def hybrid_mask(top2: np.ndarray, tile_sparse: np.ndarray, tn: int, tk: int) -> np.ndarray:
+    """Keep mask u8[N][K]: the 2:4 pattern `top2` inside the 2:4 tiles, all ones elsewhere.
+    ``tile_sparse`` is Boolean[(N/tn)*(K/tk)] in row-major tile order."""
+    n, k = top2.shape
+    sp = np.asarray(tile_sparse, dtype=bool).reshape(n // tn, k // tk)
+    elem_sparse = np.repeat(np.repeat(sp, tn, axis=0), tk, axis=1)
+    return np.where(elem_sparse, top2, np.uint8(1)).astype(np.uint8)
+
+
 def magnitude_mask(w_bits: np.ndarray, tile_sparse: np.ndarray, tn: int, tk: int) -> np.ndarray:
     """Keep/prune mask u8[N][K] (1 = keep).
 
     Dense tiles keep everything.  In a 2:4 tile every aligned group of four
     along K keeps its two largest |w|; on equal magnitudes the lower index wins.
     ``tile_sparse`` is Boolean[(N/tn)*(K/tk)] in row-major tile order."""
-    n, k = w_bits.shape
-    tiles_n, tiles_k = n // tn, k // tk
-    mag = np.abs(bf16_bits_to_f32(w_bits)).reshape(n, k // 4, 4)
-    # stable argsort on -|w| keeps the lower index first among equal magnitudes
-    order = np.argsort(-mag, axis=2, kind="stable")
-    top2 = np.zeros_like(mag, dtype=np.uint8)
-    np.put_along_axis(top2, order[:, :, :2], 1, axis=2)
-    top2 = top2.reshape(n, k)
-    sp = np.asarray(tile_sparse, dtype=bool).reshape(tiles_n, tiles_k)
-    elem_sparse = np.repeat(np.repeat(sp, tn, axis=0), tk, axis=1)
-    return np.where(elem_sparse, top2, np.uint8(1)).astype(np.uint8)
+    return hybrid_mask(magnitude_top2(w_bits), tile_sparse, tn, tk)
 
 
 # Code i0 | i1 << 2 of a 2:4 group -> index of its pattern in the order

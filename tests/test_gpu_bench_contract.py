@@ -61,3 +61,17 @@ def test_decode_workload_line():
     r = check_common(d)
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert d["cpu_baseline"] is None and d["weight_copies"] >= 2
+
+
+@pytest.mark.parametrize("wl", ["llama7b-model-prefill", "llama7b-model-decode"])
+def test_model_stack_line(wl):
+    """The whole-model linear stack, two layers: the line's contract, and the first
+    layer's products checked against the oracle on a row sample."""
+    d = run_bench("--workload", wl, "--layers", "2", "--cpu-rows", "64")
+    r = check_common(d)
+    assert d["config"]["layers"] == 2
+    assert r["bound"] == ("mfma" if wl.endswith("prefill") else "hbm")
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1
+    assert c["parity_max_rel"] <= 1e-2
+    assert d["grouped"]["ms_per_step"] > 0

@@ -9,15 +9,19 @@ Workloads (seeded, synthetic; W ~ N(0, 0.02), X ~ N(0, 1), bf16):
   * LLaMA-2-7B decode linears at M = 1, 8, 16;
   * LLaMA-2-7B prefill layer with per-matrix 2:4 fractions drawn from
     U[0.3, 1.0] around a global 90%;
-  * 13B-shaped linears at M = 2048 with 128x64, 64x128 and 64x64 tiles, from
-    all-dense to all-2:4.
+  * 13B-shaped linears at M = 2048, each at 128x64, 64x128, 64x64 and
+    128x128 tiles, from all-dense to all-2:4.
+
+Every case also checks the packing bit for bit against the oracle at its full
+tile count (up to 17 280 tiles) and the unpacked weight against the oracle's
+masked weight.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
-from sparse_gemm_patch_amd import inputs as I
+import synthetic as I
 
 pytestmark = pytest.mark.gpu
 
@@ -46,8 +50,21 @@ def sample_rows(m, seed):
     return np.unique(np.concatenate([np.arange(8), mid, np.arange(m - 8, m)]))
 
 
+def check_packing(pw, prob):
+    """Bit-exact packing at full size: every exported array equals the oracle's
+    compress (this spans the slot scan's 1024-tile chunks and the real tile
+    counts), and unpack equals the oracle's masked weight."""
+    ref = O.compress(prob.w, prob.mask, prob.tn, prob.tk)
+    got = pw.export()
+    for key in ("tile_map", "tile_slot", "dense_vals", "sparse_vals", "sparse_meta"):
+        assert np.array_equal(got[key], getattr(ref, key)), key
+    wm = pw.unpack().view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(wm, O.masked_weight(prob.w, prob.mask))
+
+
 def check_problem(P, prob, seed, repeat=True):
     pw = P.pack(dev_u16(prob.w), torch.from_numpy(prob.bits).cuda(), tile=(prob.tn, prob.tk))
+    check_packing(pw, prob)
     x = dev_u16(prob.x)
     y = pw.gemm(x)
     y2 = pw.gemm(x) if repeat else y
@@ -109,13 +126,17 @@ def test_llama7b_prefill_nonuniform(P, i):
     check_problem(P, prob, seed=400 + i, repeat=False)
 
 
-@pytest.mark.parametrize("shape,tile,frac", [
-    ((5120, 13824), (64, 128), 0.5),
-    ((13824, 5120), (128, 64), 0.9),
-    ((5120, 5120), (64, 64), 1.0),
-    ((5120, 5120), (128, 64), 0.0),
-])
-def test_13b_mixed_tiles(P, shape, tile, frac):
+# Every 13B-shaped linear at every hardware tile size (128x128 as the control),
+# the 2:4-tile fraction rotating through 0, 0.5, 0.9 and 1.0 (all-dense to
+# all-2:4); up to 17 280 tiles (13824 x 5120 in 64 x 64 tiles).
+C13B = [(shape, tile, [0.0, 0.5, 0.9, 1.0][(si + ti) % 4])
+        for si, shape in enumerate([(13824, 5120), (5120, 13824), (5120, 5120)])
+        for ti, tile in enumerate([(128, 64), (64, 128), (64, 64), (128, 128)])]
+
+
+@pytest.mark.parametrize("shape,tile,frac", C13B,
+                         ids=[f"{s[0]}x{s[1]}-{t[0]}x{t[1]}-f{f}" for s, t, f in C13B])
+def test_13b_tiles(P, shape, tile, frac):
     n, k = shape
     prob = I.make_problem("13b", 2048, n, k, tile[0], tile[1], frac=frac, cfg=5, matrix=n % 7)
     check_problem(P, prob, seed=500 + n, repeat=False)

@@ -102,3 +102,21 @@ def test_argument_errors(P):
     with pytest.raises(P.PatchError) as e:
         P.sample_mask(dev(np.zeros((8, 2), np.float32)), dev(gl), 128, 128, tile=(64, 32))
     assert e.value.status_name == "PATCH_E_SHAPE"
+
+
+@pytest.mark.parametrize("tn,tk", [(128, 128), (64, 128)])
+def test_one_hot_sample_is_the_magnitude_mask(P, tn, tk):
+    """The configuration the model-stack benchmark uses to build its masks: one-hot tile
+    logits from a chosen set of 2:4 tiles, one-hot group logits from the magnitude
+    pattern of every group, kappa 1, no noise.  The bits equal the host generator's
+    magnitude mask of the same tiles, bit for bit."""
+    import synthetic as I
+    n, k = 512, 1024
+    w = I.gen_weight(n, k, I.rng_for(90, 0, I.ROLE_W))
+    T = (n // tn) * (k // tk)
+    sel = I.choose_sparse_tiles(T, int(0.7 * T), I.rng_for(90, 0, I.ROLE_TILES))
+    tl = np.stack([~sel, sel], axis=1).astype(np.float32)
+    gl = np.eye(6, dtype=np.float32)[I.magnitude_patterns(w).astype(np.int64)]
+    bits = P.sample_mask(dev(tl), dev(gl), n, k, tile=(tn, tk), kappa=1.0).cpu().numpy()
+    want = I.pack_mask_bits(I.magnitude_mask(w, sel, tn, tk))
+    assert np.array_equal(bits, want)

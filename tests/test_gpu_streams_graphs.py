@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle as O
-from sparse_gemm_patch_amd import inputs as I
+import synthetic as I
 
 pytestmark = pytest.mark.gpu
 

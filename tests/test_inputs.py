@@ -2,7 +2,7 @@
 mask equals the mask form, ties included."""
 import numpy as np
 
-from sparse_gemm_patch_amd import inputs as I
+import synthetic as I
 
 PAIRS = [(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)]
 

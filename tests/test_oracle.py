@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from sparse_gemm_patch_amd import inputs as I
+import synthetic as I
 from conftest import read_golden
 
 TILES = [(128, 128), (128, 64), (64, 128), (64, 64)]

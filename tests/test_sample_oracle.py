@@ -108,3 +108,18 @@ def test_samples_are_valid_patch_masks(tn, tk):
     frac = float(np.mean(tmap == O.SPARSE24))
     assert 0.0 < frac < 1.0
     assert O.measured_sparsity(mask) == pytest.approx(0.5 * frac, abs=1e-12)
+
+
+def test_one_hot_sample_is_the_magnitude_mask():
+    """One-hot tile logits (from a chosen set of 2:4 tiles) and one-hot group logits (the
+    magnitude pattern of every group), kappa 1, no noise: the hard sample is exactly the
+    generator's magnitude mask of those tiles, written independently in tests/synthetic.py."""
+    import synthetic as I
+    n, k, tn, tk = 128, 256, 64, 128
+    w = I.gen_weight(n, k, I.rng_for(91, 0, I.ROLE_W))
+    T = (n // tn) * (k // tk)
+    sel = I.choose_sparse_tiles(T, 3, I.rng_for(91, 0, I.ROLE_TILES))
+    tl = np.stack([~sel, sel], axis=1).astype(np.float32)
+    gl = np.eye(6, dtype=np.float32)[I.magnitude_patterns(w).astype(np.int64)]
+    got = S.sample_mask(tl, gl, n, k, tn, tk, 1.0)
+    assert np.array_equal(got, I.magnitude_mask(w, sel, tn, tk))
