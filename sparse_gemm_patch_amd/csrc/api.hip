@@ -10,6 +10,8 @@
 #include <string>
 #include <vector>
 
+#include "layout.h"
+using namespace patch_layout;
 #include "patch_internal.h"
 
 namespace {
@@ -36,6 +38,17 @@ patch_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The integer a C caller passed for an enum argument.  Any int may arrive, and
+// reading a value outside the enumerators as the enum type is undefined in
+// C++, so the checks below work on the argument's bits.
+template <typename E>
+int enum_value(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
 
 // Device allocation with a test hook: PATCH_TEST_FAIL_ALLOC=<n> makes the n-th
 // allocation (1-based) of the calling process fail, to exercise clean-up paths.
@@ -126,8 +139,9 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
                         patch_info* info) {
   if (!out) return fail(PATCH_E_INVALID_ARG, "out is NULL");
   *out = nullptr;
-  if (order != PATCH_BITS_MSB_FIRST && order != PATCH_BITS_LSB_FIRST)
-    return fail(PATCH_E_INVALID_ARG, "bad bit order %d", (int)order);
+  const int ord = enum_value(order);
+  if (ord != PATCH_BITS_MSB_FIRST && ord != PATCH_BITS_LSB_FIRST)
+    return fail(PATCH_E_INVALID_ARG, "bad bit order %d", ord);
   patch_status st = check_tile(n, k, tile_n, tile_k);
   if (st != PATCH_OK) return st;
   const int64_t tiles = (n / tile_n) * (k / tile_k);
@@ -187,7 +201,7 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
   PATCH_TRY_ALLOC(pw->tile_desc, (size_t)tiles * sizeof(int32_t));
 
   PATCH_TRY_HIP(launch_fill_u64(scratch, 1, PATCH_NO_ERROR_LOC, s), "fill");
-  PATCH_TRY_HIP(launch_classify(mask_bits, k, (int)order, tile_n, tile_k, pw->tiles_n, pw->tiles_k, pw->tile_map,
+  PATCH_TRY_HIP(launch_classify(mask_bits, k, ord, tile_n, tile_k, pw->tiles_n, pw->tiles_k, pw->tile_map,
                                 scratch, s),
                 "classify launch");
   PATCH_TRY_HIP(launch_slot_scan(pw->tile_map, tiles, pw->tile_desc, reinterpret_cast<long long*>(scratch + 1), s),
@@ -223,7 +237,7 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
   PATCH_TRY_ALLOC(pw->sparse_vals, (size_t)pw->n_sparse * tile_n * tile_k);
   // +16 B: the streaming kernel reads 16 bytes at each lane's 8-byte code slot
   PATCH_TRY_ALLOC(pw->sparse_meta, (size_t)pw->n_sparse * tile_n * tile_k / 8 + 16);
-  PATCH_TRY_HIP(launch_compress(w, ldw, mask_bits, k, (int)order, tile_n, tile_k, pw->tiles_n, pw->tiles_k,
+  PATCH_TRY_HIP(launch_compress(w, ldw, mask_bits, k, ord, tile_n, tile_k, pw->tiles_n, pw->tiles_k,
                                 pw->tile_desc, pw->dense_vals, pw->sparse_vals, pw->sparse_meta, s),
                 "compress launch");
   // W and the mask belong to the caller and may be released as soon as we return.
@@ -264,15 +278,15 @@ static patch_status check_product(const patch_weight* w, const uint16_t* x, int6
 // Runs up to PATCH_MAX_GROUP products: those with K = 0 get a zero fill, the
 // rest one launch of the streaming kernel (m <= 16) and/or one of the tiled
 // kernel.  kernel / variant as in patch_gemm_kernel.
-static patch_status gemm_group_common(const patch_gemm_item* items, int32_t count, patch_out_dtype y_dtype,
-                                      patch_kernel kernel, int32_t variant, void* stream) {
+static patch_status gemm_group_common(const patch_gemm_item* items, int32_t count, int y_dtype, int kernel,
+                                      int32_t variant, void* stream) {
   if (count < 0 || count > PATCH_MAX_GROUP)
     return fail(PATCH_E_INVALID_ARG, "group of %d products, must be 0..%d", (int)count, PATCH_MAX_GROUP);
   if (count > 0 && !items) return fail(PATCH_E_INVALID_ARG, "items is NULL");
   if (y_dtype != PATCH_OUT_BF16 && y_dtype != PATCH_OUT_F32)
-    return fail(PATCH_E_INVALID_ARG, "bad output dtype %d", (int)y_dtype);
+    return fail(PATCH_E_INVALID_ARG, "bad output dtype %d", y_dtype);
   if (kernel != PATCH_KERNEL_AUTO && kernel != PATCH_KERNEL_TILED && kernel != PATCH_KERNEL_STREAM)
-    return fail(PATCH_E_INVALID_ARG, "bad kernel %d", (int)kernel);
+    return fail(PATCH_E_INVALID_ARG, "bad kernel %d", kernel);
   if (kernel == PATCH_KERNEL_TILED && variant > 0 && variant != 256 && variant != 192 && variant != 128 && variant != 64)
     return fail(PATCH_E_INVALID_ARG, "tiled block rows must be 256, 192, 128 or 64, got %d", (int)variant);
   if (count == 0) return ok();
@@ -324,24 +338,24 @@ static patch_status gemm_group_common(const patch_gemm_item* items, int32_t coun
 patch_status patch_gemm(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y, int64_t ldy,
                         patch_out_dtype y_dtype, void* stream) {
   const patch_gemm_item it = {w, x, m, ldx, y, ldy};
-  return gemm_group_common(&it, 1, y_dtype, PATCH_KERNEL_AUTO, 0, stream);
+  return gemm_group_common(&it, 1, enum_value(y_dtype), PATCH_KERNEL_AUTO, 0, stream);
 }
 
 patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y,
                                int64_t ldy, patch_out_dtype y_dtype, patch_kernel kernel, int32_t variant,
                                void* stream) {
   const patch_gemm_item it = {w, x, m, ldx, y, ldy};
-  return gemm_group_common(&it, 1, y_dtype, kernel, variant, stream);
+  return gemm_group_common(&it, 1, enum_value(y_dtype), enum_value(kernel), variant, stream);
 }
 
 patch_status patch_gemm_grouped(const patch_gemm_item* items, int32_t count, patch_out_dtype y_dtype,
                                 void* stream) {
-  return gemm_group_common(items, count, y_dtype, PATCH_KERNEL_AUTO, 0, stream);
+  return gemm_group_common(items, count, enum_value(y_dtype), PATCH_KERNEL_AUTO, 0, stream);
 }
 
 patch_status patch_gemm_grouped_kernel(const patch_gemm_item* items, int32_t count, patch_out_dtype y_dtype,
                                        patch_kernel kernel, int32_t variant, void* stream) {
-  return gemm_group_common(items, count, y_dtype, kernel, variant, stream);
+  return gemm_group_common(items, count, enum_value(y_dtype), enum_value(kernel), variant, stream);
 }
 
 patch_status patch_unpack(const patch_weight* w, uint16_t* w_out, int64_t ldw, void* stream) {
@@ -362,15 +376,16 @@ patch_status patch_unpack(const patch_weight* w, uint16_t* w_out, int64_t ldw, v
 
 patch_status patch_mask_unpack(const uint8_t* bits, int64_t count, patch_bit_order order, uint8_t* out,
                                void* stream) {
-  if (order != PATCH_BITS_MSB_FIRST && order != PATCH_BITS_LSB_FIRST)
-    return fail(PATCH_E_INVALID_ARG, "bad bit order %d", (int)order);
+  const int ord = enum_value(order);
+  if (ord != PATCH_BITS_MSB_FIRST && ord != PATCH_BITS_LSB_FIRST)
+    return fail(PATCH_E_INVALID_ARG, "bad bit order %d", ord);
   if (count < 0) return fail(PATCH_E_INVALID_ARG, "count < 0");
   if (count == 0) return ok();
   if (!bits || !out) return fail(PATCH_E_INVALID_ARG, "bits or out is NULL");
   int dev = 0;
   patch_status st = check_device(&dev);
   if (st != PATCH_OK) return st;
-  hipError_t e = launch_mask_unpack(bits, count, (int)order, out, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = launch_mask_unpack(bits, count, ord, out, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mask unpack launch");
   return ok();
 }
@@ -409,48 +424,28 @@ static patch_status export_impl(const patch_weight* w, uint8_t* tile_map, int32_
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy tile_desc");
     for (int64_t t = 0; t < w->tiles; ++t) tile_slot[t] >>= 1;  // desc = (slot << 1) | type
   }
-  const int64_t tn = w->tn, tk = w->tk, bt = tn / 16;
+  const int64_t tn = w->tn, tk = w->tk;
   const size_t dv = (size_t)w->n_dense * tn * tk * 2, sv = (size_t)w->n_sparse * tn * tk,
                sm = (size_t)w->n_sparse * tn * tk / 8;
-  // The device pools are in operand order (pack.hip); convert to the row-major
-  // format of the header.  Unit u = step * TN/16 + block; lane = 16 q + r.
+  // The device pools are in operand order (layout.h); convert to the row-major
+  // format of the header.
   if (dense_vals && dv) {
     std::vector<uint16_t> tmp(dv / 2);
     e = hipMemcpy(tmp.data(), w->dense_vals, dv, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy dense_vals");
-    for (int64_t s = 0; s < w->n_dense; ++s)
-      for (int64_t row = 0; row < tn; ++row)
-        for (int64_t col = 0; col < tk; ++col) {
-          const int64_t step = col / 64, cc = col % 64, q = cc / 16, within = cc % 16;
-          const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16, dw = within / 2;
-          const int64_t src = s * tn * tk + u * 1024 + (dw & 1) * 512 + lane * 8 + (dw >> 1) * 2 + (within & 1);
-          dense_vals[(s * tn + row) * tk + col] = tmp[src];
-        }
+    dense_to_row_major(tmp.data(), dense_vals, w->n_dense, tn, tk);
   }
   if (sparse_vals && sv) {
     std::vector<uint16_t> tmp(sv / 2);
     e = hipMemcpy(tmp.data(), w->sparse_vals, sv, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy sparse_vals");
-    for (int64_t s = 0; s < w->n_sparse; ++s)
-      for (int64_t row = 0; row < tn; ++row)
-        for (int64_t c = 0; c < tk / 2; ++c) {
-          const int64_t step = c / 32, q = (c % 32) / 8, j = c % 8;
-          const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16;
-          sparse_vals[(s * tn + row) * (tk / 2) + c] = tmp[s * tn * tk / 2 + u * 512 + lane * 8 + j];
-        }
+    sparse_values_to_row_major(tmp.data(), sparse_vals, w->n_sparse, tn, tk);
   }
   if (sparse_meta && sm) {
     std::vector<uint8_t> tmp(sm);
     e = hipMemcpy(tmp.data(), w->sparse_meta, sm, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy sparse_meta");
-    for (int64_t s = 0; s < w->n_sparse; ++s)
-      for (int64_t row = 0; row < tn; ++row)
-        for (int64_t b = 0; b < tk / 8; ++b) {
-          const int64_t step = b / 8, bb = b % 8, q = bb / 2;
-          const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16;
-          sparse_meta[(s * tn + row) * (tk / 8) + b] =
-              tmp[s * tn * tk / 8 + (u >> 2) * 512 + lane * 8 + (u & 3) * 2 + (bb & 1)];
-        }
+    sparse_codes_to_row_major(tmp.data(), sparse_meta, w->n_sparse, tn, tk);
   }
   return ok();
 }
@@ -458,8 +453,9 @@ static patch_status export_impl(const patch_weight* w, uint8_t* tile_map, int32_
 patch_status patch_sample_mask(const float* tile_logits, const float* tile_noise, const float* group_logits,
                                const float* group_noise, int64_t n, int64_t k, int32_t tile_n, int32_t tile_k,
                                float kappa, patch_bit_order order, uint8_t* mask_bits, void* stream) {
-  if (order != PATCH_BITS_MSB_FIRST && order != PATCH_BITS_LSB_FIRST)
-    return fail(PATCH_E_INVALID_ARG, "bad bit order %d", (int)order);
+  const int ord = enum_value(order);
+  if (ord != PATCH_BITS_MSB_FIRST && ord != PATCH_BITS_LSB_FIRST)
+    return fail(PATCH_E_INVALID_ARG, "bad bit order %d", ord);
   patch_status st = check_tile(n, k, tile_n, tile_k);
   if (st != PATCH_OK) return st;
   if (n * k == 0) return ok();
@@ -472,7 +468,7 @@ patch_status patch_sample_mask(const float* tile_logits, const float* tile_noise
   st = check_device(&dev);
   if (st != PATCH_OK) return st;
   const hipError_t e = launch_sample_mask(tile_logits, tile_noise, group_logits, group_noise, n, k, tile_n, tile_k,
-                                          kappa, order == PATCH_BITS_LSB_FIRST, mask_bits,
+                                          kappa, ord == PATCH_BITS_LSB_FIRST, mask_bits,
                                           reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "sample launch");
   return ok();
@@ -486,7 +482,7 @@ patch_status patch_import(int64_t n, int64_t k, int32_t tile_n, int32_t tile_k, 
   patch_status st = check_tile(n, k, tile_n, tile_k);
   if (st != PATCH_OK) return st;
   const int64_t tiles_n = n / tile_n, tiles_k = k / tile_k, tiles = tiles_n * tiles_k;
-  const int64_t tn = tile_n, tk = tile_k, bt = tn / 16;
+  const int64_t tn = tile_n, tk = tile_k;
   if (tiles > 0 && !tile_map) return fail(PATCH_E_INVALID_ARG, "tile_map is NULL");
   // Host-side validation of the exported format, before any device work.
   int64_t nd = 0, ns = 0;
@@ -589,28 +585,9 @@ patch_status patch_import(int64_t n, int64_t k, int32_t tile_n, int32_t tile_k, 
     for (int64_t t = 0; t < tiles; ++t)
       desc[t] = tile_map[t] == PATCH_TILE_DENSE ? (int32_t)((cd++) << 1) : (int32_t)(((cs++) << 1) | 1);
   }
-  for (int64_t sl = 0; sl < nd; ++sl)
-    for (int64_t row = 0; row < tn; ++row)
-      for (int64_t col = 0; col < tk; ++col) {
-        const int64_t step = col / 64, cc = col % 64, q = cc / 16, within = cc % 16;
-        const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16, dw = within / 2;
-        const int64_t dst = sl * tn * tk + u * 1024 + (dw & 1) * 512 + lane * 8 + (dw >> 1) * 2 + (within & 1);
-        dtmp[dst] = dense_vals[(sl * tn + row) * tk + col];
-      }
-  for (int64_t sl = 0; sl < ns; ++sl)
-    for (int64_t row = 0; row < tn; ++row) {
-      for (int64_t c = 0; c < tk / 2; ++c) {
-        const int64_t step = c / 32, q = (c % 32) / 8, j = c % 8;
-        const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16;
-        stmp[sl * tn * tk / 2 + u * 512 + lane * 8 + j] = sparse_vals[(sl * tn + row) * (tk / 2) + c];
-      }
-      for (int64_t b = 0; b < tk / 8; ++b) {
-        const int64_t step = b / 8, bb = b % 8, q = bb / 2;
-        const int64_t lane = q * 16 + row % 16, u = step * bt + row / 16;
-        mtmp[sl * tn * tk / 8 + (u >> 2) * 512 + lane * 8 + (u & 3) * 2 + (bb & 1)] =
-            sparse_meta[(sl * tn + row) * (tk / 8) + b];
-      }
-    }
+  dense_from_row_major(dense_vals, dtmp.data(), nd, tn, tk);
+  sparse_values_from_row_major(sparse_vals, stmp.data(), ns, tn, tk);
+  sparse_codes_from_row_major(sparse_meta, mtmp.data(), ns, tn, tk);
   PATCH_TRY(hipMemcpyAsync(pw->tile_map, tile_map, (size_t)tiles, hipMemcpyHostToDevice, s), "copy tile_map", 0);
   PATCH_TRY(hipMemcpyAsync(pw->tile_desc, desc.data(), (size_t)tiles * 4, hipMemcpyHostToDevice, s), "copy descriptors", 0);
   if (dv) PATCH_TRY(hipMemcpyAsync(pw->dense_vals, dtmp.data(), dv, hipMemcpyHostToDevice, s), "copy dense_vals", 0);
