@@ -253,31 +253,45 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
 // write back the whole L2 of an XCD).
 //
 // Per 256 x 256 step a CU copies 50 KiB (2:4) to 64 KiB (dense) into LDS,
-// through a fill path of about 64 bytes per clock, its waves read 136 to
-// 192 KiB back at up to 256 bytes per clock, and each SIMD runs 64 (2:4) to
-// 128 (dense) smfmacs of 16 clocks.  Measured inside the kernel, a step takes
-// about three times its smfmac time: the copy issue, the LDS read burst after
-// the barrier and the barrier itself do not overlap well.
+// its waves read 136 to 192 KiB back, and each SIMD runs 64 (2:4) to 128
+// (dense) smfmacs.  Measured on MI355X: the global -> LDS copies run at 40-48
+// bytes per clock per CU while they are issued, and a wave whose copy finds
+// the fill queue full stops issuing anything; LDS operand reads run at 128
+// bytes per clock with one reading wave per SIMD and about 165 with two; an
+// smfmac takes 17-19 clocks.  So a 90% 2:4 step needs about 1 150 clocks of
+// copy issue, 850 of LDS reads and 1 380 of matrix work per SIMD, and the
+// schedule decides how much of that overlaps (in-kernel timestamps: about
+// 2 650 clocks per step at 256 rows).
 //
 // LDS holds two stages of BM * 128 + 32 KiB:
-//   X  BM rows x 128 B; 16-byte chunk c of row r at position c ^ (r & 7).
-//      The B-operand reads (16 rows, one chunk per 16 lanes) then run at the
-//      full 256 B per clock; without the swizzle they run at a quarter of it.
+//   X  BM rows x 128 B; 16-byte chunk c of row r at position c ^ (r & 7), so
+//      that the B-operand reads (16 rows, one chunk per 16 lanes) are free of
+//      bank conflicts; without the swizzle they run at a quarter of the rate.
 //   W  four 64-row groups of 8 KiB.  A group's operands for one step are
 //      contiguous in the operand-order pools and are copied verbatim: dense 4
 //      blocks x [a0 | a1] x 1 KiB; 2:4 4 blocks x 1 KiB of values, then 512 B
 //      of codes at +4 KiB, 8 bytes per lane (one code word per block).  Lane l
 //      reads bytes 16 l .. 16 l + 15 of a block (or 8 l .. 8 l + 7 of the
 //      codes): consecutive lanes, consecutive addresses.
-// Waves 4-7 copy the whole next step (a quarter of the X rows and one W group
-// each) straight from global memory into LDS with global_load_lds, then wait
-// for their copies before the step's barrier; waves 0-3 only compute, so they
-// never stall on the fill path.  The copies are issued from inline assembly
-// (which saves and restores M0, the LDS address register): the compiler
-// cannot tell that they target the other stage, and as builtins every LDS read
-// after them would wait for them to land.  Its only other vector-memory loads
-// are the descriptor windows, waited for where they are loaded, so the
-// explicit waits are the only ones these copies need.
+// Every wave copies an eighth of the next step (BM/8 X rows and half of one W
+// group) straight from global memory into LDS with global_load_lds.  The two
+// waves of a SIMD run half a step apart: waves 0-3 copy, read and multiply
+// step i; waves 4-7 multiply step i - 1 (read at the end of the previous
+// step), then copy and read step i, so that one wave of each SIMD keeps the
+// matrix unit busy while the other stalls on copy issue or LDS reads.  Against
+// four dedicated copy waves that copy the whole step before multiplying their
+// own share this is 2-5% faster on the 256-row products (timestamps: the copy
+// waves spent about 1 000 clocks issuing before their first smfmac).  Measured
+// and dropped: the lagging waves copying before they multiply (13% slower:
+// both waves of a SIMD stall on the fill path at once), copies interleaved
+// between the smfmacs (35-40% slower: a stalled copy holds back the smfmacs
+// behind it), and three X stages with X copied two steps ahead (160 KiB of
+// LDS, 9% slower).  The copies are issued from inline assembly (which saves
+// and restores M0, the LDS address register): the compiler cannot tell that
+// they target the other stage, and as builtins every LDS read after them would
+// wait for them to land.  Its only other vector-memory loads are the
+// descriptor windows, waited for where they are loaded, so the explicit waits
+// are the only ones these copies need.
 // ------------------------------------------------------------------------
 namespace tiled {
 constexpr int BN = 256, BK = 64;
@@ -425,24 +439,22 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
   const int ns = tn == 128 ? 7 : 6;   // log2(TN)
   const int bt = tn >> 4;             // 16-row blocks per tile
 
-  // ---- copy roles: waves 4-7 (the second wave on each SIMD) copy the whole
-  // step; waves 0-3 only compute, so they start their smfmacs right after the
-  // barrier while the copies queue up behind the vector-memory path.  Copy
-  // wave c = wave - 4 takes X rows BM/4 c .. +BM/4-1 (8 rows per 1 KiB copy,
-  // logical chunk (lane & 7) ^ (row & 7); rows past M clamp to M - 1, they only
-  // feed Y rows that are never stored) and W group c (rows n0 + 64 c .. +63).
-  const bool copier = wave >= 4;
-  const int cw = wave & 3;
-  constexpr int XC = BM / 32;  // X copies per copy wave
+  // ---- copy roles: every wave copies an eighth of the next step.  Wave w:
+  // X rows BM/8 w .. +BM/8-1 (8 rows per 1 KiB copy), and half (w >> 2) of W
+  // group (w & 3): dense 4 of its 8 KiB, 2:4 two value blocks and 256 B of codes.
+  const int cw = wave & 3, chalf = wave >> 2;
+  constexpr int XC = BM / 64;  // X copies per wave
   const uint8_t* xblk = reinterpret_cast<const uint8_t*>(x + m0 * ldx);
-  uint32_t xoff[XC];
-#pragma unroll
-  for (int j = 0; j < XC; ++j) {
-    const int row = BM / 4 * cw + 8 * j + (lane >> 3);
+  // byte offset of this lane's 16 bytes in X copy j: row BM/8 wave + 8 j + lane / 8
+  // of the block (rows past M read row M - 1: they only feed Y rows that are never
+  // stored), logical chunk (lane & 7) ^ (row & 7); recomputed per copy, which
+  // costs a few VALU operations and saves the registers of a table
+  auto xoff = [&](int j) -> uint32_t {
+    const int row = BM / 8 * wave + 8 * j + (lane >> 3);
     int64_t gm = m0 + row;
     if (gm > m - 1) gm = m - 1;
-    xoff[j] = (uint32_t)(((gm - m0) * ldx + 8 * ((lane & 7) ^ xswz(row))) * 2);
-  }
+    return (uint32_t)(((gm - m0) * ldx + 8 * ((lane & 7) ^ xswz(row))) * 2);
+  };
   const int64_t gn0 = n0 + 64 * cw;
   const bool g_ok = gn0 < n;
   const int64_t g_desc = (gn0 >> ns) * tiles_k;
@@ -451,40 +463,37 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
   const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(sparse_vals);
   const uint32_t loff16 = lane * 16, loff4 = lane * 4;
 
-  // A group's 8 KiB: dense = 8 blocks of 1 KiB; 2:4 = 4 value blocks and 512 B
-  // of codes at +4 KiB (two 256 B copies).
   int32_t gd = 0;  // descriptor window of the copy group's tile row
   int gwin = -1;
-  auto issue = [&](int step, int stage) {
-    if (!copier) return;
-    const uint32_t st = lds_base + stage * STAGE_BYTES;
-#pragma unroll
-    for (int j = 0; j < XC; ++j) dma16(xblk + step * 128, xoff[j], st + (BM / 4 * cw + 8 * j) * 128);
-    const uint32_t g = st + X_BYTES + cw * G_BYTES;
-    if (!g_ok) return;  // group past N
+  // descriptor window for the copies of `step`; loaded (and waited for) before any copy of the step
+  auto copy_desc = [&](int step) -> int32_t {
     const int col = step >> ks;
-    if ((col >> 6) != gwin) {
+    if (g_ok && (col >> 6) != gwin) {
       gwin = col >> 6;
       gd = desc_window(tile_desc, g_desc, tiles_k, gwin, lane);
-      // wait for the window here, once: passed through asm, gd no longer looks like
-      // a pending load, so the per-step readlane needs no wait (which would also
-      // wait for every copy in flight)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       asm volatile("" : "+v"(gd));
     }
-    const int32_t d = __builtin_amdgcn_readlane(gd, col & 63);
+    return __builtin_amdgcn_readlane(gd, col & 63);
+  };
+  auto issue = [&](int step, int stage, int32_t d) {
+    const uint32_t st = lds_base + stage * STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < XC; ++j) dma16(xblk + step * 128, xoff(j), st + (BM / 8 * wave + 8 * j) * 128);
+    const uint32_t g = st + X_BYTES + cw * G_BYTES;
+    if (!g_ok) return;  // group past N
     const int64_t slot = d >> 1;
     const int64_t u0 = (step & ks) * bt + g_blk;  // first operand unit of the group
     if ((d & 1) == PATCH_TILE_DENSE) {
-      const uint8_t* src = dsrc + (slot * tn * tk + u0 * 1024) * 2;
+      const uint8_t* src = dsrc + (slot * tn * tk + u0 * 1024) * 2 + 4096 * chalf;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dma16(src + 1024 * j, loff16, g + 1024 * j);
+      for (int j = 0; j < 4; ++j) dma16(src + 1024 * j, loff16, g + 4096 * chalf + 1024 * j);
     } else {
-      const uint8_t* src = ssrc + slot * tn * tk + u0 * 1024;
+      const uint8_t* src = ssrc + slot * tn * tk + u0 * 1024 + 2048 * chalf;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(src + 1024 * j, loff16, g + 1024 * j);
-      const uint8_t* mp = sparse_meta + slot * tn * (tk >> 3) + (u0 >> 2) * 512;
-      dma4(mp, loff4, g + 4096);
-      dma4(mp + 256, loff4, g + 4096 + 256);
+      for (int j = 0; j < 2; ++j) dma16(src + 1024 * j, loff16, g + 2048 * chalf + 1024 * j);
+      const uint8_t* mp = sparse_meta + slot * tn * (tk >> 3) + (u0 >> 2) * 512 + 256 * chalf;
+      dma4(mp, loff4, g + 4096 + 256 * chalf);
     }
   };
 
@@ -501,9 +510,12 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
 
   uint64_t dn0 = 0, dn1 = 0;  // bit j: column 64 cwin + j of this wave's tile rows is dense
   int cwin = -1;
-  auto compute = [&](int step, int stage) {
-    const uint8_t* cur = lds + stage * STAGE_BYTES;
-    const int col = step >> ks;
+  int d0 = -1, d1 = -1;
+  bf16x16 b[XB];
+  bf16x8 a0[8], a1[8];
+  int ix[2][2];  // per W group: the code words of blocks (0, 1) and (2, 3)
+  // dense / 2:4 bits of the window of tile columns holding `col`
+  auto compute_window = [&](int col) {
     if ((col >> 6) != cwin) {
       cwin = col >> 6;
       const int32_t v0 = hok0 ? desc_window(tile_desc, hdesc0, tiles_k, cwin, lane) : 1;
@@ -511,16 +523,18 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
       dn0 = __builtin_amdgcn_ballot_w64((v0 & 1) == PATCH_TILE_DENSE);
       dn1 = __builtin_amdgcn_ballot_w64((v1 & 1) == PATCH_TILE_DENSE);
     }
-    const int d0 = hok0 ? (int)((dn0 >> (col & 63)) & 1) : -1;
-    const int d1 = hok1 ? (int)((dn1 >> (col & 63)) & 1) : -1;
-    bf16x16 b[XB];
+  };
+  auto load_ops = [&](int step, int stage) {
+    const uint8_t* cur = lds + stage * STAGE_BYTES;
+    const int col = step >> ks;
+    compute_window(col);
+    d0 = hok0 ? (int)((dn0 >> (col & 63)) & 1) : -1;
+    d1 = hok1 ? (int)((dn1 >> (col & 63)) & 1) : -1;
 #pragma unroll
     for (int bm = 0; bm < XB; ++bm) {
       const int r = BM / 4 * wm + 16 * bm + r16;
       b[bm] = cat16(lds8(cur + r * 128 + ((q ^ xswz(r)) << 4)), lds8(cur + r * 128 + (((4 + q) ^ xswz(r)) << 4)));
     }
-    bf16x8 a0[8], a1[8];
-    int ix[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int dh = h ? d1 : d0;
@@ -530,18 +544,18 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
         for (int b4 = 0; b4 < 4; ++b4) {
           a0[4 * h + b4] = lds8(g + 2048 * b4 + lane * 16);
           a1[4 * h + b4] = lds8(g + 2048 * b4 + 1024 + lane * 16);
-          ix[4 * h + b4] = 0x44444444;  // kept positions 0 and 1 of every group, in both halves
         }
+        ix[h][0] = ix[h][1] = 0x44444444;  // kept positions 0 and 1 of every group, in both halves
       } else if (dh == 0) {
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) a0[4 * h + b4] = lds8(g + 1024 * b4 + lane * 16);
         const uint2 c = *reinterpret_cast<const uint2*>(g + 4096 + 8 * lane);
-        ix[4 * h + 0] = (int)c.x;
-        ix[4 * h + 1] = (int)c.x;
-        ix[4 * h + 2] = (int)c.y;
-        ix[4 * h + 3] = (int)c.y;
+        ix[h][0] = (int)c.x;
+        ix[h][1] = (int)c.y;
       }
     }
+  };
+  auto mma = [&]() {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int dh = h ? d1 : d0;
@@ -551,9 +565,8 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) {
           const int bn = 4 * h + b4;
-          // odd blocks of a 2:4 group take the upper 16 bits of their code word
-          acc[bn][bm] = b4 & 1 ? __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b[bm], acc[bn][bm], ix[bn], 0, 1)
-                               : __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b[bm], acc[bn][bm], ix[bn], 0, 0);
+          acc[bn][bm] = b4 & 1 ? __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b[bm], acc[bn][bm], ix[h][b4 >> 1], 0, 1)
+                               : __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[bn], b[bm], acc[bn][bm], ix[h][b4 >> 1], 0, 0);
         }
       if (dh > 0) {  // kept positions 2 and 3 of every group
 #pragma unroll
@@ -567,11 +580,37 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
     }
   };
 
-  if (nsteps > 0) issue(0, 0);
-  for (int i = 0; i < nsteps; ++i) {
-    step_barrier();  // step i has landed in stage i & 1; stage (i + 1) & 1 is free
-    if (i + 1 < nsteps) issue(i + 1, (i + 1) & 1);
-    compute(i, i & 1);
+  // Two waves per SIMD (wave w and w + 4) run half a step apart: after the
+  // barrier of step i, waves 0-3 issue their copies of step i + 1, read step i
+  // and multiply it; waves 4-7 multiply step i - 1 (read before the barrier),
+  // issue their copies and read step i.  Copies of step i + 1 go to the stage
+  // that every wave finished reading before the barrier.
+  // 64-row blocks run two workgroups per CU (128 VGPRs): both wave groups keep
+  // the same order there, and the other workgroup on the CU fills the gaps.
+  // The first descriptor windows are loaded before any copy is in flight (a
+  // wait for them would otherwise also wait for the copies).
+  constexpr bool LAG = BM > 64;
+  if (nsteps > 0) {
+    compute_window(0);
+    issue(0, 0, copy_desc(0));
+  }
+  if (!LAG || wn == 0) {
+    for (int i = 0; i < nsteps; ++i) {
+      const int32_t dnext = i + 1 < nsteps ? copy_desc(i + 1) : 0;
+      step_barrier();
+      if (i + 1 < nsteps) issue(i + 1, (i + 1) & 1, dnext);
+      load_ops(i, i & 1);
+      mma();
+    }
+  } else if (nsteps > 0) {
+    for (int i = 0; i < nsteps; ++i) {
+      const int32_t dnext = i + 1 < nsteps ? copy_desc(i + 1) : 0;
+      step_barrier();
+      if (i > 0) mma();
+      if (i + 1 < nsteps) issue(i + 1, (i + 1) & 1, dnext);
+      load_ops(i, i & 1);
+    }
+    mma();
   }
 
   // After the last barrier every wave is done with step nsteps - 2, and no copy
@@ -588,7 +627,7 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
 // its next block.  The barrier between blocks keeps the next block's first
 // copies off LDS that slower waves still read.
 template <bool F32, int BM>
-__global__ __launch_bounds__(512, 1) void k_gemm_tiled(const gemm_group g) {
+__global__ __launch_bounds__(512, BM == 64 ? 4 : 1) void k_gemm_tiled(const gemm_group g) {
   for (int slot = blockIdx.x; slot < g.total; slot += gridDim.x) {
     tiled_block<F32, BM>(g, slot);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
