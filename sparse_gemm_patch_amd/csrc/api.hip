@@ -120,6 +120,7 @@ void fill_info(const patch_weight* w, patch_info* info) {
 
 void free_weight(patch_weight* w) {
   if (!w) return;
+  delete[] w->row_dense_prefix;
   dev_free(w->tile_map);
   dev_free(w->tile_desc);
   dev_free(w->dense_vals);
@@ -129,6 +130,28 @@ void free_weight(patch_weight* w) {
 }
 
 }  // namespace
+
+bool set_cost_prefix(patch_weight* w, const uint8_t* tile_map_host) {
+  int64_t* p = new (std::nothrow) int64_t[w->tiles_n + 1];
+  if (!p) return false;
+  p[0] = 0;
+  for (int64_t i = 0; i < w->tiles_n; ++i) {
+    int64_t d = 0;
+    for (int64_t j = 0; j < w->tiles_k; ++j) d += tile_map_host[i * w->tiles_k + j] == PATCH_TILE_DENSE;
+    p[i + 1] = p[i] + d;
+  }
+  delete[] w->row_dense_prefix;
+  w->row_dense_prefix = p;
+  return true;
+}
+
+double row_cost(const patch_weight* w, int64_t r0, int64_t r1) {
+  if (r1 > w->tiles_n) r1 = w->tiles_n;
+  if (r0 >= r1 || w->tiles_k == 0) return PATCH_STEP_COST_DENSE;
+  const double tiles = (double)(r1 - r0) * (double)w->tiles_k;
+  const double dense = (double)(w->row_dense_prefix[r1] - w->row_dense_prefix[r0]);
+  return (dense * PATCH_STEP_COST_DENSE + (tiles - dense) * PATCH_STEP_COST_24) / tiles;
+}
 
 extern "C" {
 
@@ -168,6 +191,10 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
   pw->tiles = tiles;
 
   if (tiles == 0) {
+    if (!set_cost_prefix(pw, nullptr)) {
+      free_weight(pw);
+      return fail(PATCH_E_NOMEM, "host allocation failed");
+    }
     if (info) fill_info(pw, info);
     *out = pw;
     return ok();
@@ -207,7 +234,17 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
   PATCH_TRY_HIP(launch_slot_scan(pw->tile_map, tiles, pw->tile_desc, reinterpret_cast<long long*>(scratch + 1), s),
                 "slot scan launch");
   unsigned long long host[3] = {0, 0, 0};
+  std::vector<uint8_t> map_host;
+  try {
+    map_host.resize((size_t)tiles);
+  } catch (const std::bad_alloc&) {
+    dev_free(scratch);
+    free_weight(pw);
+    return fail(PATCH_E_NOMEM, "host allocation failed");
+  }
   PATCH_TRY_HIP(hipMemcpyAsync(host, scratch, sizeof(host), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+  PATCH_TRY_HIP(hipMemcpyAsync(map_host.data(), pw->tile_map, (size_t)tiles, hipMemcpyDeviceToHost, s),
+                "hipMemcpyAsync");
   PATCH_TRY_HIP(hipStreamSynchronize(s), "hipStreamSynchronize");
 
   if (host[0] != PATCH_NO_ERROR_LOC) {
@@ -232,6 +269,11 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
   }
   pw->n_dense = (int64_t)host[1];
   pw->n_sparse = (int64_t)host[2];
+  if (!set_cost_prefix(pw, map_host.data())) {
+    dev_free(scratch);
+    free_weight(pw);
+    return fail(PATCH_E_NOMEM, "host allocation failed");
+  }
 
   PATCH_TRY_ALLOC(pw->dense_vals, (size_t)pw->n_dense * tile_n * tile_k * 2);
   PATCH_TRY_ALLOC(pw->sparse_vals, (size_t)pw->n_sparse * tile_n * tile_k);
@@ -542,6 +584,10 @@ patch_status patch_import(int64_t n, int64_t k, int32_t tile_n, int32_t tile_k, 
   pw->tiles = tiles;
   pw->n_dense = nd;
   pw->n_sparse = ns;
+  if (!set_cost_prefix(pw, tile_map)) {
+    free_weight(pw);
+    return fail(PATCH_E_NOMEM, "host allocation failed");
+  }
   if (tiles == 0) {
     if (info) fill_info(pw, info);
     *out = pw;

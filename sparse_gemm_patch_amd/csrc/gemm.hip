@@ -22,6 +22,8 @@
 
 #include <atomic>
 #include <climits>
+#include <cstdio>
+#include <cstdlib>
 
 namespace {
 
@@ -308,7 +310,7 @@ __device__ __forceinline__ void step_barrier() {
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ int xswz(int r) { return r & 7; }
 
-// Output block of this workgroup.  The dispatcher deals workgroup i to XCD
+// Output block of this workgroup (W rows from n_begin on).  The dispatcher deals workgroup i to XCD
 // i % 8; renumbering so that each XCD owns a contiguous range of blocks, walked
 // in groups of group_n block columns (m fastest inside a group), makes the
 // workgroups resident on one XCD cover a compact region and share their W and
@@ -316,9 +318,9 @@ __device__ __forceinline__ int xswz(int r) { return r & 7; }
 // bid: the workgroup's index inside its product, whose first workgroup is a
 // multiple of 8 in the launch (so bid % 8 is still its XCD).
 template <int BM, int BN>
-__device__ __forceinline__ void block_origin(int64_t n, int64_t m, int bid, int group_n, int64_t& n0,
-                                             int64_t& m0) {
-  const int nbn = (int)((n + BN - 1) / BN), nbm = (int)((m + BM - 1) / BM);
+__device__ __forceinline__ void block_origin(int64_t n_begin, int64_t n, int64_t m, int bid, int group_n,
+                                             int64_t& n0, int64_t& m0) {
+  const int nbn = (int)((n - n_begin + BN - 1) / BN), nbm = (int)((m + BM - 1) / BM);
   const int total = nbn * nbm;
   const int xcd = bid & 7, local = bid >> 3, base = total >> 3, rem = total & 7;
   const int id = xcd < rem ? xcd * (base + 1) + local : rem * (base + 1) + (xcd - rem) * base + local;
@@ -326,7 +328,7 @@ __device__ __forceinline__ void block_origin(int64_t n, int64_t m, int bid, int 
   const int group = id / per_group, in_group = id % per_group;
   const int first = group * group_n;
   const int width = nbn - first < group_n ? nbn - first : group_n;
-  n0 = (int64_t)(first + in_group % width) * BN;
+  n0 = n_begin + (int64_t)(first + in_group % width) * BN;
   m0 = (int64_t)(in_group / width) * BM;
 }
 
@@ -404,14 +406,10 @@ __device__ __forceinline__ void store_block(const f32x4 (&acc)[4 * GW][XB], uint
   }
 }
 
-// One output block of k_gemm_tiled: workgroup slot `slot` of the launch.
+// One output block of k_gemm_tiled: block `local` of entry P of the launch.
 template <bool F32, int BM>
-__device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
+__device__ __forceinline__ void tiled_block(const gemm_problem& P, int local) {
   using namespace tiled;
-  int local;
-  const int pi = find_problem(g, slot, local);
-  if (pi < 0) return;
-  const gemm_problem& P = g.p[pi];
   const const_desc_ptr tile_desc = (const_desc_ptr)P.tile_desc;
   const uint16_t* __restrict__ dense_vals = P.dense_vals;
   const uint16_t* __restrict__ sparse_vals = P.sparse_vals;
@@ -433,7 +431,7 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
   const int wn = wave >> 2, wm = wave & 3;
   const int q = lane >> 4, r16 = lane & 15;
   int64_t n0, m0;
-  block_origin<BM, BN>(n, m, local, P.group_n, n0, m0);
+  block_origin<BM, BN>(P.n_begin, n, m, local, P.group_n, n0, m0);
   const int nsteps = (int)(k / BK);
   const int ks = tk == 128;           // 64-wide K steps per tile column: 1 << ks
   const int ns = tn == 128 ? 7 : 6;   // log2(TN)
@@ -626,10 +624,23 @@ __device__ __forceinline__ void tiled_block(const gemm_group& g, int slot) {
 // and a block's Y stores drain while the same workgroup copies and multiplies
 // its next block.  The barrier between blocks keeps the next block's first
 // copies off LDS that slower waves still read.
+//
+// The 256-row instance also runs entries of 192-row blocks (gemm_problem.bm):
+// the launcher may cut a product's last, ragged round of 256-row blocks into a
+// round of 192-row ones in the same launch (see plan_tail).
 template <bool F32, int BM>
 __global__ __launch_bounds__(512, BM == 64 ? 4 : 1) void k_gemm_tiled(const gemm_group g) {
   for (int slot = blockIdx.x; slot < g.total; slot += gridDim.x) {
-    tiled_block<F32, BM>(g, slot);
+    int local;
+    const int pi = find_problem(g, slot, local);
+    if (pi >= 0) {
+      if constexpr (BM == 256) {
+        if (g.p[pi].bm == 192) tiled_block<F32, 192>(g.p[pi], local);
+        else tiled_block<F32, 256>(g.p[pi], local);
+      } else {
+        tiled_block<F32, BM>(g.p[pi], local);
+      }
+    }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
@@ -694,7 +705,7 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
   asm volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t n0, m0;
-  block_origin<BM, BN>(n, m, local, P.group_n, n0, m0);
+  block_origin<BM, BN>(P.n_begin, n, m, local, P.group_n, n0, m0);
   const int nsteps = (int)(k / 64);
   const int nstages = (nsteps + KS - 1) / KS;  // stage loads, KS K steps each (the last may hold fewer)
   const int ks = tk == 128;
@@ -930,6 +941,9 @@ gemm_problem make_problem(const patch_weight* w, const uint16_t* x, int64_t m, i
   const double tiles = (double)(w->n_dense + w->n_sparse);
   p.w_bytes = tiles > 0 ? (float)((2.0 * w->n_dense + 1.125 * w->n_sparse) / tiles) : 2.0f;
   p.group_n = 4;
+  p.n_begin = 0;
+  p.bm = 0;
+  p.mix = (float)row_cost(w, 0, w->tiles_n);
   return p;
 }
 
@@ -996,8 +1010,9 @@ int persistent_grid(const void* kernel, int threads, int lds_bytes, std::atomic<
 void group_width(gemm_group& g, int bm, int bn, int per_xcd) {
   for (int i = 0; i < g.count; ++i) {
     gemm_problem& p = g.p[i];
-    const int64_t nbn = (p.n + bn - 1) / bn;
-    const double xrow = 2.0 * bm * (double)p.k, wcol = (double)p.w_bytes * bn * (double)p.k;
+    const int64_t nbn = (p.n - p.n_begin + bn - 1) / bn;
+    const int ebm = p.bm > 0 ? p.bm : bm;
+    const double xrow = 2.0 * ebm * (double)p.k, wcol = (double)p.w_bytes * bn * (double)p.k;
     int best = 1;
     double best_b = 0;
     for (int w = 1; w <= 32 && w <= nbn; w *= 2) {
@@ -1012,27 +1027,122 @@ void group_width(gemm_group& g, int bm, int bn, int per_xcd) {
   }
 }
 
+// Relative cost of one workgroup: block height over its measured efficiency
+// (smaller blocks move more LDS bytes per flop), times the K steps.
+double block_cost(int bm, int64_t k) {
+  // measured in whole rounds on the 8192x2048 and 4096x4096 products at M = 4096
+  // (192: from the 8192x2048, 4096x4096 and 5120x5120 products, 0.84-0.96)
+  const double eff = bm == 256 ? 1.0 : bm == 192 ? 0.92 : bm == 128 ? 0.96 : 0.68;
+  return bm / 256.0 / eff * (double)(k / 64);
+}
+
+// Slots s in [0, x) with s % G == w.
+inline int64_t slots_below(int64_t x, int w, int G) { return x > w ? (x - 1 - w) / G + 1 : 0; }
+
+// Cost-balanced tail of a launch of 256-row blocks.  Workgroup w of a
+// persistent grid of G runs slots w, w + G, ...; when the last entry's blocks
+// leave a ragged last round, its first block columns keep 256-row blocks and
+// the rest become 192-row blocks (two entries of one launch), if that lowers
+// the estimated makespan by 2% or more.  A block's cost is block_cost times the
+// mean step cost of its entry's tile rows (row_cost: the dense / 2:4 mix from
+// the packed weight's cost prefix).  The split points tried put the end of the
+// 256-row blocks on a round boundary.  Example: 11008 x 4096 at M = 4096 is
+// 688 blocks of 256 x 256 on 256 workgroups (2.69 rounds); 32 block columns
+// (512 blocks, 2 rounds) stay, the other 11 become 242 blocks of 192 rows that
+// share the third round.
+void plan_tail(gemm_group& g, int G) {
+  constexpr int MAXG = 4096;
+  if (g.count == 0 || g.count >= PATCH_MAX_GROUP || G <= 0 || G > MAXG) return;
+  static thread_local double load[MAXG];
+  for (int w = 0; w < G; ++w) load[w] = 0;
+  int64_t s0 = 0;
+  for (int i = 0; i + 1 < g.count; ++i) {
+    const gemm_problem& p = g.p[i];
+    const int64_t blocks = ((p.n - p.n_begin + 255) / 256) * ((p.m + 255) / 256);
+    const double c = block_cost(256, p.k) * p.mix;
+    for (int w = 0; w < G; ++w) load[w] += c * (double)(slots_below(s0 + blocks, w, G) - slots_below(s0, w, G));
+    s0 += (blocks + 7) / 8 * 8;
+  }
+  gemm_problem& last = g.p[g.count - 1];
+  const int64_t nbn = (last.n - last.n_begin + 255) / 256, nbm = (last.m + 255) / 256, nbm2 = (last.m + 191) / 192;
+  const double c256 = block_cost(256, last.k) * last.mix, c192 = block_cost(192, last.k) * last.mix;
+  // makespan with the first ca block columns in 256-row blocks, the rest in 192-row ones
+  auto makespan = [&](int64_t ca) {
+    const int64_t a = ca * nbm, sb = s0 + (a + 7) / 8 * 8, b = (nbn - ca) * nbm2;
+    double worst = 0;
+    for (int w = 0; w < G; ++w) {
+      const double t = load[w] + c256 * (double)(slots_below(s0 + a, w, G) - slots_below(s0, w, G)) +
+                       c192 * (double)(slots_below(sb + b, w, G) - slots_below(sb, w, G));
+      worst = t > worst ? t : worst;
+    }
+    return worst;
+  };
+  const double base = makespan(nbn);
+  int64_t best_ca = nbn;
+  double best = base;
+  for (int64_t r = 1; r * G <= s0 + nbn * nbm + G; ++r) {
+    const int64_t ca = (r * G - s0) / nbm;
+    if (ca < 1 || ca >= nbn) continue;
+    const double t = makespan(ca);
+    if (t < best) {
+      best = t;
+      best_ca = ca;
+    }
+  }
+  if (best_ca == nbn || best > 0.98 * base) return;
+  gemm_problem tail = last;
+  tail.n_begin = last.n_begin + best_ca * 256;
+  tail.bm = 192;
+  last.n = tail.n_begin;
+  g.p[g.count++] = tail;
+}
+
+// PATCH_LOG=1 in the environment prints every tiled launch's plan to stderr:
+// block height, grid and the entries with their W-row ranges.
+bool log_launches() {
+  static const bool on = [] {
+    const char* e = getenv("PATCH_LOG");
+    return e && *e && *e != '0';
+  }();
+  return on;
+}
+
+void log_plan(const char* kernel, const gemm_group& g, int grid) {
+  if (!log_launches()) return;
+  fprintf(stderr, "patch: %s grid %d slots %d", kernel, grid, (int)g.total);
+  for (int i = 0; i < g.count; ++i)
+    fprintf(stderr, " | rows %lld..%lld m %lld k %lld bm %d blocks %d", (long long)g.p[i].n_begin,
+            (long long)g.p[i].n, (long long)g.p[i].m, (long long)g.p[i].k, g.p[i].bm, g.p[i].blocks);
+  fprintf(stderr, "\n");
+}
+
 template <bool F32, int BM>
-hipError_t launch_tiled_bm(gemm_group& g, hipStream_t s) {
+hipError_t launch_tiled_bm(gemm_group& g, bool plan, hipStream_t s) {
   constexpr int lds_bytes = tiled::STAGES * tiled::stage_bytes<BM>();
   static std::atomic<bool> lds_allowed[64] = {};
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(&k_gemm_tiled<F32, BM>), lds_bytes, lds_allowed);
   if (e != hipSuccess) return e;
-  // Each product's workgroups start at a multiple of 8 (the XCD count), so the
+  static std::atomic<int> resident[64] = {};
+  const int held = persistent_grid(reinterpret_cast<const void*>(&k_gemm_tiled<F32, BM>), 512, lds_bytes, resident,
+                                   INT32_MAX);
+  if (held < 0) return hipErrorInvalidDevice;
+  for (int i = 0; i < g.count; ++i) g.p[i].bm = BM;
+  if (BM == 256 && plan) plan_tail(g, held);
+  // Each entry's workgroups start at a multiple of 8 (the XCD count), so the
   // block order inside it stays XCD-aware; padding slots are skipped.
   int64_t total = 0;
   for (int i = 0; i < g.count; ++i) {
     g.p[i].block0 = (int32_t)total;
-    g.p[i].blocks = (int32_t)(((g.p[i].n + tiled::BN - 1) / tiled::BN) * ((g.p[i].m + BM - 1) / BM));
+    g.p[i].blocks = (int32_t)(((g.p[i].n - g.p[i].n_begin + tiled::BN - 1) / tiled::BN) *
+                              ((g.p[i].m + g.p[i].bm - 1) / g.p[i].bm));
     total += (g.p[i].blocks + 7) / 8 * 8;
   }
   if (total == 0) return hipSuccess;
   if (total > INT32_MAX) return hipErrorInvalidValue;  // block numbers are 32-bit
-  static std::atomic<int> resident[64] = {};
-  const int grid = persistent_grid(reinterpret_cast<const void*>(&k_gemm_tiled<F32, BM>), 512, lds_bytes, resident, total);
-  if (grid < 0) return hipErrorInvalidDevice;
+  const int grid = total < held ? (int)total : held;
   g.total = (int32_t)total;
   group_width(g, BM, tiled::BN, grid / 8);
+  log_plan("k_gemm_tiled", g, grid);
   hipLaunchKernelGGL((k_gemm_tiled<F32, BM>), dim3((unsigned)grid), dim3(512), lds_bytes, s, g);
   return hipGetLastError();
 }
@@ -1058,7 +1168,9 @@ hipError_t launch_ws(gemm_group& g, hipStream_t s) {
       persistent_grid(reinterpret_cast<const void*>(&k_gemm_ws<F32, BM, NG, KS>), 64 * wsk::WAVES, lds_bytes, resident, total);
   if (grid < 0) return hipErrorInvalidDevice;
   g.total = (int32_t)total;
+  for (int i = 0; i < g.count; ++i) g.p[i].bm = BM;
   group_width(g, BM, BN, grid / 8);
+  log_plan("k_gemm_ws", g, grid);
   hipLaunchKernelGGL((k_gemm_ws<F32, BM, NG, KS>), dim3((unsigned)grid), dim3(64 * wsk::WAVES), lds_bytes, s, g);
   return hipGetLastError();
 }
@@ -1070,20 +1182,13 @@ int64_t padded_blocks(const gemm_group& g, int bm, int bn) {
   return total;
 }
 
-// Relative cost of one workgroup: block height over its measured efficiency
-// (smaller blocks move more LDS bytes per flop), times the K steps.
-double block_cost(int bm, int64_t k) {
-  // measured in whole rounds on the 8192x2048 and 4096x4096 products at M = 4096
-  // (192: from the 8192x2048, 4096x4096 and 5120x5120 products, 0.84-0.96)
-  const double eff = bm == 256 ? 1.0 : bm == 192 ? 0.92 : bm == 128 ? 0.96 : 0.68;
-  return bm / 256.0 / eff * (double)(k / 64);
-}
 }  // namespace
 
 int tiled_block_m(const gemm_group& g) {
   // Estimated time of each block height: rounds of 256 workgroups when every
   // product has the same K, else total cost spread over the CUs but never less
-  // than the longest workgroup.
+  // than the longest workgroup.  Block costs carry each product's dense / 2:4
+  // mix (gemm_problem.mix).
   const int bms[4] = {256, 192, 128, 64};
   bool same_k = true;
   for (int i = 1; i < g.count; ++i) same_k = same_k && g.p[i].k == g.p[0].k;
@@ -1094,9 +1199,10 @@ int tiled_block_m(const gemm_group& g) {
     double cost = 0, longest = 0;
     for (int i = 0; i < g.count; ++i) {
       const int64_t b = ((g.p[i].n + tiled::BN - 1) / tiled::BN) * ((g.p[i].m + bms[j] - 1) / bms[j]);
+      const double c = block_cost(bms[j], g.p[i].k) * g.p[i].mix;
       blocks += b;
-      cost += b * block_cost(bms[j], g.p[i].k);
-      longest = longest > block_cost(bms[j], g.p[i].k) ? longest : block_cost(bms[j], g.p[i].k);
+      cost += b * c;
+      longest = longest > c ? longest : c;
     }
     const double t = same_k ? (double)((blocks + 255) / 256) * longest : (cost / 256 > longest ? cost / 256 : longest);
     if (j == 0 || t < best_t - 1e-9) {
@@ -1108,9 +1214,11 @@ int tiled_block_m(const gemm_group& g) {
 }
 
 hipError_t launch_tiled_group(gemm_group& g, int out_f32, int block_m, hipStream_t s) {
-  // longest K first, so that the most expensive workgroups are dispatched first
+  // most expensive blocks first (K steps times the dense / 2:4 mix), so that
+  // the cheaper ones fill the last round
+  auto key = [](const gemm_problem& p) { return (double)p.k * p.mix; };
   for (int i = 1; i < g.count; ++i)
-    for (int j = i; j > 0 && g.p[j].k > g.p[j - 1].k; --j) {
+    for (int j = i; j > 0 && key(g.p[j]) > key(g.p[j - 1]); --j) {
       const gemm_problem t = g.p[j];
       g.p[j] = g.p[j - 1];
       g.p[j - 1] = t;
@@ -1127,13 +1235,13 @@ hipError_t launch_tiled_group(gemm_group& g, int out_f32, int block_m, hipStream
         return out_f32 ? launch_ws<true, 64, 2, 2>(g, s) : launch_ws<false, 64, 2, 2>(g, s);
       if (padded_blocks(g, 64, 256) <= 256)
         return out_f32 ? launch_ws<true, 64, 4, 1>(g, s) : launch_ws<false, 64, 4, 1>(g, s);
-      return out_f32 ? launch_tiled_bm<true, 64>(g, s) : launch_tiled_bm<false, 64>(g, s);
+      return out_f32 ? launch_tiled_bm<true, 64>(g, false, s) : launch_tiled_bm<false, 64>(g, false, s);
     case 128:
       return out_f32 ? launch_ws<true, 128, 4, 1>(g, s) : launch_ws<false, 128, 4, 1>(g, s);
     case 192:
-      return out_f32 ? launch_tiled_bm<true, 192>(g, s) : launch_tiled_bm<false, 192>(g, s);
+      return out_f32 ? launch_tiled_bm<true, 192>(g, false, s) : launch_tiled_bm<false, 192>(g, false, s);
     default:
-      return out_f32 ? launch_tiled_bm<true, 256>(g, s) : launch_tiled_bm<false, 256>(g, s);
+      return out_f32 ? launch_tiled_bm<true, 256>(g, block_m <= 0, s) : launch_tiled_bm<false, 256>(g, block_m <= 0, s);
   }
 }
 

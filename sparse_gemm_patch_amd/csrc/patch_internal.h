@@ -23,7 +23,21 @@ struct patch_weight {
   uint16_t* dense_vals;  // [D][TN][TK]
   uint16_t* sparse_vals; // [S][TN][TK/2]
   uint8_t* sparse_meta;  // [S][TN][TK/8]
+  // Host: row_dense_prefix[i] = dense tiles in tile rows 0 .. i-1 (tiles_n + 1
+  // entries), the cost prefix the GEMM launcher schedules by.
+  int64_t* row_dense_prefix;
 };
+
+// Relative time of one 64-wide K step of a 64-row W group in the tiled
+// kernels: dense 1, 2:4 0.84 (in-kernel timestamps on MI355X, 256-row blocks,
+// 90% against 0% 2:4 tiles: 2 650 against 3 150 clocks per step).
+#define PATCH_STEP_COST_DENSE 1.0
+#define PATCH_STEP_COST_24 0.84
+// Mean relative step cost of tile rows [r0, r1) of w (1 = all dense).
+double row_cost(const patch_weight* w, int64_t r0, int64_t r1);
+// Fills w->row_dense_prefix from a host copy of the tile map; false if the
+// host allocation fails.
+bool set_cost_prefix(patch_weight* w, const uint8_t* tile_map_host);
 
 // Sentinel for "no invalid group found".
 #define PATCH_NO_ERROR_LOC 0xFFFFFFFFFFFFFFFFull
@@ -67,6 +81,9 @@ struct gemm_problem {
   int32_t blocks;  // its workgroups (the launch may pad after them)
   float w_bytes;   // packed bytes per weight element (2 dense, 1.125 for 2:4, mean over tiles)
   int32_t group_n; // tiled kernels: block columns per group of the block order
+  int64_t n_begin; // this entry covers W rows / Y columns n_begin .. n - 1
+  int32_t bm;      // tiled kernels: X rows per block of this entry (set by the launcher)
+  float mix;       // mean relative step cost of the entry's W rows (host scheduling only)
 };
 struct gemm_group {
   int32_t count;
