@@ -154,10 +154,13 @@ patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t
  * A transformer layer applies several linears to the same or to different
  * inputs (the card's model is LLaMA-3.2-1B: q, k, v, o, gate, up and down
  * projections per layer, each with its own PATCH mask).  Each item is the
- * patch_gemm of its own handle, X and Y; the whole group runs as at most one
- * launch of each kernel (STREAM for the items with m <= 16, TILED for the
- * rest) plus a zero fill per item with K = 0, so small projections share the
- * chip instead of running one after another.
+ * patch_gemm of its own handle, X and Y.  Items with m <= 16 share one launch
+ * of the STREAM kernel; TILED items that fill the GPU on their own (at least
+ * one 256 x 256 output block per compute unit) get a launch each, and the
+ * other TILED items share one launch, so small projections share the chip
+ * instead of running one after another; an item with K = 0 gets a zero fill.
+ * With patch_gemm_grouped_kernel and a forced kernel, all items of that
+ * kernel share one launch.
  *
  *   items    host, `count` items; read during the call only.
  *   count    0 .. 16 (0 is a no-op).

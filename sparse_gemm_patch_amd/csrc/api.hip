@@ -91,6 +91,21 @@ patch_status check_device(int* dev_out) {
   return PATCH_OK;
 }
 
+// Compute units of a device, cached per device ordinal.
+hipError_t compute_units(int dev, int* cus) {
+  static std::atomic<int> cache[64];
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return hipSuccess;
+    }
+  }
+  const hipError_t e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && dev >= 0 && dev < 64) cache[dev].store(*cus, std::memory_order_relaxed);
+  return e;
+}
+
 patch_status check_tile(int64_t n, int64_t k, int32_t tn, int32_t tk) {
   if ((tn != 64 && tn != 128) || (tk != 64 && tk != 128))
     return fail(PATCH_E_SHAPE, "tile %dx%d: each side must be 64 or 128", tn, tk);
@@ -369,6 +384,30 @@ static patch_status gemm_group_common(const patch_gemm_item* items, int32_t coun
   if (streamed.count) {
     e = launch_stream_group(streamed, f32, s);
     if (e != hipSuccess) return hip_fail(e, "gemm launch (streaming kernel)");
+  }
+  if (tiled.count > 1 && kernel == PATCH_KERNEL_AUTO) {
+    // A product with at least one 256 x 256 block per CU fills the GPU on its
+    // own: it gets a launch of its own, with its own block height and tail
+    // plan, as a solo patch_gemm would.  Only the under-filled products share a
+    // launch, which is where sharing gains (measured on the 32-layer LLaMA-2-7B
+    // prefill stack: sharing launches between its full-size products was 4%
+    // slower than launching them one by one).
+    int cus = 0;
+    e = compute_units(dev, &cus);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    gemm_group small = {};
+    for (int i = 0; i < tiled.count; ++i) {
+      const gemm_problem& p = tiled.p[i];
+      if (((p.n + 255) / 256) * ((p.m + 255) / 256) >= cus) {
+        gemm_group one = {};
+        one.p[one.count++] = p;
+        e = launch_tiled_group(one, f32, 0, s);
+        if (e != hipSuccess) return hip_fail(e, "gemm launch (tiled kernel)");
+      } else {
+        small.p[small.count++] = p;
+      }
+    }
+    tiled = small;
   }
   if (tiled.count) {
     e = launch_tiled_group(tiled, f32, kernel == PATCH_KERNEL_AUTO ? 0 : variant, s);
