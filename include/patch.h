@@ -318,7 +318,50 @@ patch_status patch_import(int64_t n, int64_t k, int32_t tile_n, int32_t tile_k, 
                           const uint16_t* dense_vals, const uint16_t* sparse_vals, const uint8_t* sparse_meta,
                           void* stream, patch_weight** out, patch_info* info);
 
-/* Free a handle and its device memory (NULL is a no-op).  The caller must make
+/*
+ * patch_pack_noalloc -- patch_pack for callers that cannot allocate memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the caller provides the device pools and the host storage of the
+ * handle, and the library allocates nothing, on the device or the host.
+ *
+ * Same validation, packed format, status codes and blocking as patch_pack,
+ * with these differences:
+ *   tile_map, tile_desc  device, tiles and 4 * tiles bytes (tiles =
+ *            (n/tile_n) * (k/tile_k)); tile_desc 16-byte aligned.
+ *   dense_vals / sparse_vals / sparse_meta  device pools of dense_bytes,
+ *            sparse_bytes and meta_bytes bytes, 16-byte aligned.  After
+ *            classification they must hold 2 D TN TK, S TN TK and S TN TK / 8 +
+ *            16 bytes (D, S: dense and 2:4 tiles; sizes for every tile dense,
+ *            2 n k, and every tile 2:4, n k and n k / 8 + 16, always suffice);
+ *            otherwise PATCH_E_INVALID_ARG and nothing is compressed.
+ *   storage  host memory the handle is built in; *out points into it.
+ * The caller owns storage and every pool and must keep them alive while the
+ * handle is used; patch_destroy on this handle frees nothing.  The handle
+ * works with every other entry point.  Its rows are scheduled at the weight's
+ * mean dense / 2:4 mix (patch_pack keeps a per-row count on the host).
+ *
+ * Validation uses a fixed 32-byte scratch in device memory, one per GPU,
+ * reserved when the library is loaded and held until the process ends; it does
+ * not grow with the weight, so no size is refused for it.  Every call on one
+ * GPU reuses it: calls that overlap on the same GPU (different host threads or
+ * streams) race and must be serialised by the caller.
+ */
+typedef struct {
+  uint64_t words[64];
+} patch_weight_storage;
+
+patch_status patch_pack_noalloc(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
+                                const uint8_t* mask_bits, patch_bit_order order,
+                                int32_t tile_n, int32_t tile_k, void* stream,
+                                uint8_t* tile_map, int32_t* tile_desc,
+                                uint16_t* dense_vals, int64_t dense_bytes,
+                                uint16_t* sparse_vals, int64_t sparse_bytes,
+                                uint8_t* sparse_meta, int64_t meta_bytes,
+                                patch_weight_storage* storage, patch_weight** out,
+                                patch_info* info);
+
+/* Free a handle and its device memory (NULL is a no-op; a handle made by
+ * patch_pack_noalloc owns nothing and is left alone).  The caller must make
  * sure no work using it is still in flight. */
 void patch_destroy(patch_weight* w);
 

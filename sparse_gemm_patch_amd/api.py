@@ -25,7 +25,7 @@ DENSE, SPARSE24 = 0, 1
 # Exported entry points; kept in step with include/patch.h.
 SYMBOLS = ("patch_pack", "patch_gemm", "patch_gemm_kernel", "patch_gemm_grouped", "patch_gemm_grouped_kernel",
            "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_import",
-           "patch_sample_mask", "patch_destroy", "patch_last_error")
+           "patch_sample_mask", "patch_pack_noalloc", "patch_destroy", "patch_last_error")
 MAX_GROUP = 16
 
 
@@ -39,6 +39,11 @@ class PatchInfo(ctypes.Structure):
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class WeightStorage(ctypes.Structure):
+    """Host storage of a handle made by patch_pack_noalloc (patch_weight_storage)."""
+    _fields_ = [("words", ctypes.c_uint64 * 64)]
 
 
 class GemmItem(ctypes.Structure):
@@ -83,13 +88,15 @@ def load() -> ctypes.CDLL:
     L.patch_export.argtypes = [vp, vp, vp, vp, vp, vp]
     L.patch_import.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(PatchInfo)]
     L.patch_sample_mask.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, ctypes.c_float, ctypes.c_int, vp, vp]
+    L.patch_pack_noalloc.argtypes = [vp, i64, i64, i64, vp, ctypes.c_int, i32, i32, vp, vp, vp, vp, i64, vp, i64, vp,
+                                     i64, vp, ctypes.POINTER(vp), ctypes.POINTER(PatchInfo)]
     L.patch_destroy.argtypes = [vp]
     L.patch_destroy.restype = None
     L.patch_last_error.argtypes = []
     L.patch_last_error.restype = ctypes.c_char_p
     for name in ("patch_pack", "patch_gemm", "patch_gemm_kernel", "patch_gemm_grouped", "patch_gemm_grouped_kernel",
                  "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_import",
-                 "patch_sample_mask"):
+                 "patch_sample_mask", "patch_pack_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L

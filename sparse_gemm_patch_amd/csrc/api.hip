@@ -134,7 +134,7 @@ void fill_info(const patch_weight* w, patch_info* info) {
 }
 
 void free_weight(patch_weight* w) {
-  if (!w) return;
+  if (!w || w->borrowed) return;
   delete[] w->row_dense_prefix;
   dev_free(w->tile_map);
   dev_free(w->tile_desc);
@@ -163,6 +163,10 @@ bool set_cost_prefix(patch_weight* w, const uint8_t* tile_map_host) {
 double row_cost(const patch_weight* w, int64_t r0, int64_t r1) {
   if (r1 > w->tiles_n) r1 = w->tiles_n;
   if (r0 >= r1 || w->tiles_k == 0) return PATCH_STEP_COST_DENSE;
+  if (!w->row_dense_prefix) {  // no per-row counts: the weight's mean mix
+    const double t = (double)(w->n_dense + w->n_sparse);
+    return t > 0 ? (w->n_dense * PATCH_STEP_COST_DENSE + w->n_sparse * PATCH_STEP_COST_24) / t : PATCH_STEP_COST_DENSE;
+  }
   const double tiles = (double)(r1 - r0) * (double)w->tiles_k;
   const double dense = (double)(w->row_dense_prefix[r1] - w->row_dense_prefix[r0]);
   return (dense * PATCH_STEP_COST_DENSE + (tiles - dense) * PATCH_STEP_COST_24) / tiles;
@@ -687,5 +691,135 @@ patch_status patch_import(int64_t n, int64_t k, int32_t tile_n, int32_t tile_k, 
 }
 
 void patch_destroy(patch_weight* w) { free_weight(w); }
+
+}  // extern "C"
+
+// ---- allocation-free packing ------------------------------------------------
+// Validation scratch of patch_pack_noalloc: [0] first invalid group, [1] dense
+// tiles, [2] 2:4 tiles.  One copy per GPU, held until the process ends; every
+// call on a GPU reuses it (so calls that overlap on one GPU race).  In host code
+// the array's name is only a stand-in: kernels get the per-device address
+// hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned long long scratch[PATCH_PACK_SCRATCH_WORDS];
+
+namespace {
+
+// Device address of `scratch` on device dev, looked up once per device (with
+// that device current, as here: every entry point runs on the current device).
+hipError_t scratch_address(int dev, unsigned long long** out) {
+  static std::atomic<unsigned long long*> addr[64] = {};
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  unsigned long long* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* q = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    p = static_cast<unsigned long long*>(q);
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+patch_status patch_pack_noalloc(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, const uint8_t* mask_bits,
+                                patch_bit_order order, int32_t tile_n, int32_t tile_k, void* stream,
+                                uint8_t* tile_map, int32_t* tile_desc, uint16_t* dense_vals, int64_t dense_bytes,
+                                uint16_t* sparse_vals, int64_t sparse_bytes, uint8_t* sparse_meta,
+                                int64_t meta_bytes, patch_weight_storage* storage, patch_weight** out,
+                                patch_info* info) {
+  static_assert(sizeof(patch_weight) <= sizeof(patch_weight_storage), "handle fits the caller's storage");
+  static_assert(alignof(patch_weight) <= alignof(patch_weight_storage), "handle alignment");
+  if (!out) return fail(PATCH_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!storage) return fail(PATCH_E_INVALID_ARG, "storage is NULL");
+  const int ord = enum_value(order);
+  if (ord != PATCH_BITS_MSB_FIRST && ord != PATCH_BITS_LSB_FIRST)
+    return fail(PATCH_E_INVALID_ARG, "bad bit order %d", ord);
+  patch_status st = check_tile(n, k, tile_n, tile_k);
+  if (st != PATCH_OK) return st;
+  const int64_t tiles = (n / tile_n) * (k / tile_k);
+  if (tiles > 0) {
+    if (!w || !mask_bits || !tile_map || !tile_desc) return fail(PATCH_E_INVALID_ARG, "NULL pointer");
+    if (!aligned16(w) || !aligned16(mask_bits) || !aligned16(tile_desc))
+      return fail(PATCH_E_INVALID_ARG, "w, mask_bits and tile_desc must be 16-byte aligned");
+    if (ldw < k || ldw % 8) return fail(PATCH_E_INVALID_ARG, "ldw %lld must be >= k and a multiple of 8", (long long)ldw);
+    if (dense_bytes < 0 || sparse_bytes < 0 || meta_bytes < 0) return fail(PATCH_E_INVALID_ARG, "negative pool size");
+    if ((dense_bytes && (!dense_vals || !aligned16(dense_vals))) ||
+        (sparse_bytes && (!sparse_vals || !aligned16(sparse_vals))) ||
+        (meta_bytes && (!sparse_meta || !aligned16(sparse_meta))))
+      return fail(PATCH_E_INVALID_ARG, "pools must be 16-byte aligned and non-NULL when their size is not 0");
+  }
+  int dev = 0;
+  st = check_device(&dev);
+  if (st != PATCH_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  patch_weight* pw = new (storage) patch_weight();
+  pw->borrowed = true;
+  pw->device = dev;
+  pw->n = n;
+  pw->k = k;
+  pw->tn = tile_n;
+  pw->tk = tile_k;
+  pw->tiles_n = n / tile_n;
+  pw->tiles_k = k / tile_k;
+  pw->tiles = tiles;
+  if (tiles == 0) {
+    if (info) fill_info(pw, info);
+    *out = pw;
+    return ok();
+  }
+  unsigned long long* sc = nullptr;
+  hipError_t e = scratch_address(dev, &sc);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress");
+  pw->tile_map = tile_map;
+  pw->tile_desc = tile_desc;
+  // the first-error word must start at "no error"; the counts are written, not accumulated
+  if ((e = launch_fill_u64(sc, 1, PATCH_NO_ERROR_LOC, s)) != hipSuccess) return hip_fail(e, "fill launch");
+  if ((e = launch_classify(mask_bits, k, ord, tile_n, tile_k, pw->tiles_n, pw->tiles_k, tile_map, sc, s)) != hipSuccess)
+    return hip_fail(e, "classify launch");
+  if ((e = launch_slot_scan(tile_map, tiles, tile_desc, reinterpret_cast<long long*>(sc + 1), s)) != hipSuccess)
+    return hip_fail(e, "slot scan launch");
+  unsigned long long host[3] = {0, 0, 0};
+  if ((e = hipMemcpyAsync(host, sc, sizeof(host), hipMemcpyDeviceToHost, s)) != hipSuccess)
+    return hip_fail(e, "hipMemcpyAsync");
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  if (host[0] != PATCH_NO_ERROR_LOC) {
+    const int64_t per_tile = (int64_t)tile_n * tile_k / 4;
+    const int64_t loc = (int64_t)host[0];
+    if (info) {
+      fill_info(pw, info);
+      info->n_dense = info->n_sparse = 0;
+      info->bad_tile = loc / per_tile;
+      info->bad_row = (loc % per_tile) / (tile_k / 4);
+      info->bad_group = (loc % per_tile) % (tile_k / 4);
+    }
+    return fail(PATCH_E_MASK, "mask is not tile-wise dense / 2:4: tile %lld, row %lld in tile, group %lld along K",
+                (long long)(loc / per_tile), (long long)((loc % per_tile) / (tile_k / 4)),
+                (long long)((loc % per_tile) % (tile_k / 4)));
+  }
+  pw->n_dense = (int64_t)host[1];
+  pw->n_sparse = (int64_t)host[2];
+  const int64_t need_d = pw->n_dense * tile_n * tile_k * 2, need_s = pw->n_sparse * tile_n * tile_k,
+                need_m = pw->n_sparse * tile_n * tile_k / 8 + (pw->n_sparse ? 16 : 0);
+  if (dense_bytes < need_d || sparse_bytes < need_s || meta_bytes < need_m)
+    return fail(PATCH_E_INVALID_ARG,
+                "pools too small for %lld dense and %lld 2:4 tiles: need %lld, %lld and %lld bytes, have %lld, %lld "
+                "and %lld", (long long)pw->n_dense, (long long)pw->n_sparse, (long long)need_d, (long long)need_s,
+                (long long)need_m, (long long)dense_bytes, (long long)sparse_bytes, (long long)meta_bytes);
+  pw->dense_vals = dense_vals;
+  pw->sparse_vals = sparse_vals;
+  pw->sparse_meta = sparse_meta;
+  if ((e = launch_compress(w, ldw, mask_bits, k, ord, tile_n, tile_k, pw->tiles_n, pw->tiles_k, tile_desc, dense_vals,
+                           sparse_vals, sparse_meta, s)) != hipSuccess)
+    return hip_fail(e, "compress launch");
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  if (info) fill_info(pw, info);
+  *out = pw;
+  return ok();
+}
 
 }  // extern "C"

@@ -24,8 +24,12 @@ struct patch_weight {
   uint16_t* sparse_vals; // [S][TN][TK/2]
   uint8_t* sparse_meta;  // [S][TN][TK/8]
   // Host: row_dense_prefix[i] = dense tiles in tile rows 0 .. i-1 (tiles_n + 1
-  // entries), the cost prefix the GEMM launcher schedules by.
+  // entries), the cost prefix the GEMM launcher schedules by (NULL for a handle
+  // made by patch_pack_noalloc: its rows then count at the weight's mean mix).
   int64_t* row_dense_prefix;
+  // Made by patch_pack_noalloc: the struct and the pools belong to the caller,
+  // and patch_destroy frees nothing.
+  bool borrowed;
 };
 
 // Relative time of one 64-wide K step of a 64-row W group in the tiled
@@ -38,6 +42,9 @@ double row_cost(const patch_weight* w, int64_t r0, int64_t r1);
 // Fills w->row_dense_prefix from a host copy of the tile map; false if the
 // host allocation fails.
 bool set_cost_prefix(patch_weight* w, const uint8_t* tile_map_host);
+
+// Words of the per-GPU validation scratch of patch_pack_noalloc.
+#define PATCH_PACK_SCRATCH_WORDS 4
 
 // Sentinel for "no invalid group found".
 #define PATCH_NO_ERROR_LOC 0xFFFFFFFFFFFFFFFFull

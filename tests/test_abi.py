@@ -36,7 +36,8 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
-@pytest.mark.parametrize("cls,cname", [(api.PatchInfo, "patch_info"), (api.GemmItem, "patch_gemm_item")])
+@pytest.mark.parametrize("cls,cname", [(api.PatchInfo, "patch_info"), (api.GemmItem, "patch_gemm_item"),
+                                       (api.WeightStorage, "patch_weight_storage")])
 def test_struct_layout_matches_header(tmp_path, cls, cname):
     """ctypes' structs must match what a C compiler makes of include/patch.h."""
     import shutil
@@ -179,3 +180,23 @@ def test_sample_mask_argument_errors(lib):
 def test_header_max_ldx():
     text = open(HEADER).read()
     assert re.search(r"#define PATCH_MAX_LDX 4194304LL", text)
+
+
+def test_pack_noalloc_argument_errors(lib):
+    """Rejected before any HIP call; *out is cleared."""
+    st = api.WeightStorage()
+    h = ctypes.c_void_p(0xDEAD)
+    vp = ctypes.c_void_p
+
+    def call(n=128, k=128, tn=64, tk=64, order=0, storage=True, out=True, w=1 << 20):
+        h.value = 0xDEAD
+        return lib.patch_pack_noalloc(vp(w), n, k, k, vp(1 << 20), order, tn, tk, None, vp(1 << 20), vp(1 << 20),
+                                      vp(1 << 20), 1 << 16, vp(1 << 20), 1 << 16, vp(1 << 20), 1 << 16,
+                                      ctypes.byref(st) if storage else None, ctypes.byref(h) if out else None, None)
+    assert call(out=False) == 1
+    assert call(storage=False) == 1 and h.value is None
+    assert call(order=3) == 1 and h.value is None
+    assert call(tn=32) == 2 and h.value is None
+    assert call(n=100) == 2
+    assert call(w=0) == 1
+    assert call(w=(1 << 20) + 2) == 1
