@@ -41,7 +41,7 @@ extern "C" {
 typedef enum {
   PATCH_OK = 0,
   PATCH_E_INVALID_ARG = 1, /* null / misaligned pointer, bad enum, bad leading dimension */
-  PATCH_E_SHAPE = 2,       /* tile not in {64,128}^2, or N % TN != 0, or K % TK != 0 */
+  PATCH_E_SHAPE = 2,       /* tile not in {64,128}^2, N % TN != 0, K % TK != 0, or N*K > 2^31 - 1 */
   PATCH_E_MASK = 3,        /* some tile is neither all-dense nor exactly 2:4 along K */
   PATCH_E_HIP = 4,         /* a HIP runtime call failed (message has hipGetErrorString) */
   PATCH_E_NOMEM = 5,       /* device allocation failed; nothing is leaked */
@@ -57,6 +57,12 @@ typedef enum { PATCH_OUT_BF16 = 0, PATCH_OUT_F32 = 1 } patch_out_dtype;
 
 /* Largest X leading dimension (elements) patch_gemm accepts: 2^22. */
 #define PATCH_MAX_LDX 4194304LL
+
+/* Largest weight (N * K elements) patch_pack, patch_pack_noalloc, patch_import
+ * and patch_sample_mask accept: 2^31 - 1.  The GEMM kernels address the packed
+ * pools with 32-bit byte offsets; the largest linear of a 70B-class model holds
+ * about 2^28 weights. */
+#define PATCH_MAX_WEIGHTS 2147483647LL
 
 typedef enum { PATCH_TILE_DENSE = 0, PATCH_TILE_SPARSE24 = 1 } patch_tile_type;
 

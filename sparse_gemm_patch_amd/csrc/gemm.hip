@@ -65,17 +65,45 @@ __device__ __forceinline__ void store4(void* y, int64_t ldy, int64_t m, int64_t 
 // global -> LDS copy of 16 (or 4) bytes per lane from base + off (base
 // wave-uniform, off a 32-bit per-lane byte offset); lane i writes LDS bytes
 // lds_addr + 16 i (4 i).  lds_addr must be wave-uniform.  A scalar base keeps
-// one VGPR per copy stream instead of a 64-bit address.
+// one VGPR per copy stream instead of a 64-bit address.  The LDS address goes
+// in M0, which the asm declares clobbered (the compiler sets it again where it
+// needs it) instead of saving and restoring it around every copy.
 __device__ __forceinline__ bf16x8 lds8(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               : : "s"(lds_addr), "v"(off), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               : : "s"(lds_addr), "v"(off), "s"(base) : "memory", "m0");
+}
+// The same copy with M0 saved and restored around it: three more scalar
+// instructions per copy.  k_gemm_tiled issues its X and dense-tile copies this
+// way: issued back to back with one M0 write each, they made all-dense steps
+// 4-8% slower (the 8192 x 2048 product at M = 4096, the 13824 x 5120 one at
+// M = 2048), with no gain on 2:4 steps; spread out, a wave reaches a full fill
+// queue later.
+__device__ __forceinline__ void dma16_paced(const void* base, uint32_t off, uint32_t lds_addr) {
   uint32_t saved;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
                : "=&s"(saved) : "s"(lds_addr), "v"(off), "s"(base) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(lds_addr), "v"(off), "s"(base) : "memory");
+// A run of copies that share one M0: the instruction's immediate offset moves
+// the global and the LDS address alike, so consecutive 1 KiB blocks of a pool
+// need one M0 write between them.  set_m0 must precede the first dma*_at of
+// the run, with no other copy in between.
+__device__ __forceinline__ void set_m0(uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" : : "s"(lds_addr) : "memory", "m0");
+}
+template <int IMM>
+__device__ __forceinline__ void dma16_at(const void* base, uint32_t off) {
+  static_assert(IMM >= 0 && IMM < 4096, "immediate offset range");
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" : : "v"(off), "s"(base), "i"(IMM) : "memory", "m0");
+}
+template <int IMM>
+__device__ __forceinline__ void dma4_at(const void* base, uint32_t off) {
+  static_assert(IMM >= 0 && IMM < 4096, "immediate offset range");
+  asm volatile("global_load_lds_dword %0, %1 offset:%2" : : "v"(off), "s"(base), "i"(IMM) : "memory", "m0");
 }
 // ------------------------------------------------------------------------
 // Streaming kernel for M <= 16 (decode).
@@ -288,10 +316,13 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
 // both waves of a SIMD stall on the fill path at once), copies interleaved
 // between the smfmacs (35-40% slower: a stalled copy holds back the smfmacs
 // behind it), and three X stages with X copied two steps ahead (160 KiB of
-// LDS, 9% slower).  The copies are issued from inline assembly (which saves
-// and restores M0, the LDS address register): the compiler cannot tell that
-// they target the other stage, and as builtins every LDS read after them would
-// wait for them to land.  Its only other vector-memory loads are the
+// LDS, 9% slower).  The copies are issued from inline assembly: the compiler
+// cannot tell that they target the other stage, and as builtins every LDS read
+// after them would wait for them to land.  The two 1 KiB value blocks of a 2:4
+// group share one write of M0 (the LDS address register) through the
+// instruction's immediate offset: with about 40% fewer scalar instructions per
+// step the 2:4-heavy products run 2-4% faster.  X and dense-tile copies keep
+// one M0 write per copy, with M0 saved and restored (see dma16_paced).  Its only other vector-memory loads are the
 // descriptor windows, waited for where they are loaded, so the explicit waits
 // are the only ones these copies need.
 // ------------------------------------------------------------------------
@@ -460,6 +491,7 @@ __device__ __forceinline__ void tiled_block(const gemm_problem& P, int local) {
   const uint8_t* dsrc = reinterpret_cast<const uint8_t*>(dense_vals);
   const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(sparse_vals);
   const uint32_t loff16 = lane * 16, loff4 = lane * 4;
+  const uint32_t tile_elems = (uint32_t)(tn * tk);
 
   int32_t gd = 0;  // descriptor window of the copy group's tile row
   int gwin = -1;
@@ -477,20 +509,22 @@ __device__ __forceinline__ void tiled_block(const gemm_problem& P, int local) {
   auto issue = [&](int step, int stage, int32_t d) {
     const uint32_t st = lds_base + stage * STAGE_BYTES;
 #pragma unroll
-    for (int j = 0; j < XC; ++j) dma16(xblk + step * 128, xoff(j), st + (BM / 8 * wave + 8 * j) * 128);
+    for (int j = 0; j < XC; ++j) dma16_paced(xblk + step * 128, xoff(j), st + (BM / 8 * wave + 8 * j) * 128);
     const uint32_t g = st + X_BYTES + cw * G_BYTES;
     if (!g_ok) return;  // group past N
-    const int64_t slot = d >> 1;
-    const int64_t u0 = (step & ks) * bt + g_blk;  // first operand unit of the group
+    // pool offsets in 32 bits: every pool is below 4 GiB (checked at pack and import)
+    const uint32_t slot = (uint32_t)d >> 1;
+    const uint32_t u0 = (uint32_t)((step & ks) * bt + g_blk);  // first operand unit of the group
     if ((d & 1) == PATCH_TILE_DENSE) {
-      const uint8_t* src = dsrc + (slot * tn * tk + u0 * 1024) * 2 + 4096 * chalf;
+      const uint8_t* src = dsrc + (slot * tile_elems + u0 * 1024u) * 2u + 4096u * chalf;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(src + 1024 * j, loff16, g + 4096 * chalf + 1024 * j);
+      for (int j = 0; j < 4; ++j) dma16_paced(src + 1024 * j, loff16, g + 4096 * chalf + 1024 * j);
     } else {
-      const uint8_t* src = ssrc + slot * tn * tk + u0 * 1024 + 2048 * chalf;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) dma16(src + 1024 * j, loff16, g + 2048 * chalf + 1024 * j);
-      const uint8_t* mp = sparse_meta + slot * tn * (tk >> 3) + (u0 >> 2) * 512 + 256 * chalf;
+      const uint8_t* src = ssrc + slot * tile_elems + u0 * 1024u + 2048u * chalf;
+      set_m0(g + 2048 * chalf);
+      dma16_at<0>(src, loff16);
+      dma16_at<1024>(src, loff16);
+      const uint8_t* mp = sparse_meta + slot * (tile_elems >> 3) + (u0 >> 2) * 512u + 256u * chalf;
       dma4(mp, loff4, g + 4096 + 256 * chalf);
     }
   };
@@ -652,7 +686,10 @@ __global__ __launch_bounds__(512, BM == 64 ? 4 : 1) void k_gemm_tiled(const gemm
 // waves 8-11 (one per SIMD) only copy, two steps ahead through three LDS
 // stages (48 KiB each at 128 rows, 40 at 64).  A wave that issues copies
 // stalls while the per-CU fill path drains; here no computing wave ever does,
-// and the third stage hides the copies' latency.
+// and the third stage hides the copies' latency.  A copy wave writes M0 once
+// per run of consecutive 1 KiB pool blocks (immediate offsets for the rest), so
+// it issues its copies with fewer scalar instructions: 6-16% faster on the
+// 512 x 2048 products at M = 4096, 1-2% on the 2048-wide ones.
 // ------------------------------------------------------------------------
 namespace wsk {
 constexpr int STAGES = 3, WAVES = 12;
@@ -737,6 +774,7 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
     const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(P.sparse_vals);
     const uint8_t* msrc = P.sparse_meta;
     const uint32_t loff16 = lane * 16, loff4 = lane * 4;
+    const uint32_t tile_elems = (uint32_t)(tn * tk);
     // copies of K step `step` into the LDS bytes at st
     auto issue_step = [&](int step, uint32_t st) -> int {
 #pragma unroll
@@ -744,20 +782,32 @@ __device__ __forceinline__ void ws_block(const gemm_group& g, int slot) {
       const uint32_t gl = st + X_BYTES + cw * G_BYTES;
       if (!g_ok) return XC;
       const int32_t d = tile_desc[g_desc + (step >> ks)];
-      const int64_t slot = d >> 1;
-      const int64_t u0 = (step & ks) * bt + g_blk;
+      const uint32_t slot = (uint32_t)d >> 1;  // pools are below 4 GiB
+      const uint32_t u0 = (uint32_t)((step & ks) * bt + g_blk);
       if ((d & 1) == PATCH_TILE_DENSE) {
-        const uint8_t* src = dsrc + (slot * tn * tk + u0 * 1024) * 2;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dma16(src + 1024 * j, loff16, gl + 1024 * j);
+        const uint8_t* src = dsrc + (slot * tile_elems + u0 * 1024u) * 2u;
+        set_m0(gl);
+        dma16_at<0>(src, loff16);
+        dma16_at<1024>(src, loff16);
+        dma16_at<2048>(src, loff16);
+        dma16_at<3072>(src, loff16);
+        set_m0(gl + 4096);
+        dma16_at<0>(src + 4096, loff16);
+        dma16_at<1024>(src + 4096, loff16);
+        dma16_at<2048>(src + 4096, loff16);
+        dma16_at<3072>(src + 4096, loff16);
         return XC + 8;
       }
-      const uint8_t* src = ssrc + slot * tn * tk + u0 * 1024;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(src + 1024 * j, loff16, gl + 1024 * j);
-      const uint8_t* mp = msrc + slot * tn * (tk >> 3) + (u0 >> 2) * 512;
-      dma4(mp, loff4, gl + 4096);
-      dma4(mp + 256, loff4, gl + 4096 + 256);
+      const uint8_t* src = ssrc + slot * tile_elems + u0 * 1024u;
+      set_m0(gl);
+      dma16_at<0>(src, loff16);
+      dma16_at<1024>(src, loff16);
+      dma16_at<2048>(src, loff16);
+      dma16_at<3072>(src, loff16);
+      const uint8_t* mp = msrc + slot * (tile_elems >> 3) + (u0 >> 2) * 512u;
+      set_m0(gl + 4096);
+      dma4_at<0>(mp, loff4);
+      dma4_at<256>(mp, loff4);
       return XC + 6;
     };
     // copies of stage load t (K steps KS t ..) into LDS stage `stage`

@@ -198,5 +198,8 @@ def test_pack_noalloc_argument_errors(lib):
     assert call(order=3) == 1 and h.value is None
     assert call(tn=32) == 2 and h.value is None
     assert call(n=100) == 2
+    # more than PATCH_MAX_WEIGHTS (2^31 - 1) weights: the pools' 32-bit offsets would wrap
+    assert call(n=65536, k=32768) == 2 and h.value is None
+    assert b"2^31" in lib.patch_last_error()
     assert call(w=0) == 1
     assert call(w=(1 << 20) + 2) == 1
