@@ -506,10 +506,13 @@ __device__ __forceinline__ void tiled_block(const gemm_problem& P, int local) {
     }
     return __builtin_amdgcn_readlane(gd, col & 63);
   };
-  auto issue = [&](int step, int stage, int32_t d) {
+  auto issue_x = [&](int step, int stage) {
     const uint32_t st = lds_base + stage * STAGE_BYTES;
 #pragma unroll
     for (int j = 0; j < XC; ++j) dma16_paced(xblk + step * 128, xoff(j), st + (BM / 8 * wave + 8 * j) * 128);
+  };
+  auto issue_w = [&](int step, int stage, int32_t d) {
+    const uint32_t st = lds_base + stage * STAGE_BYTES;
     const uint32_t g = st + X_BYTES + cw * G_BYTES;
     if (!g_ok) return;  // group past N
     // pool offsets in 32 bits: every pool is below 4 GiB (checked at pack and import)
@@ -527,6 +530,10 @@ __device__ __forceinline__ void tiled_block(const gemm_problem& P, int local) {
       const uint8_t* mp = sparse_meta + slot * (tile_elems >> 3) + (u0 >> 2) * 512u + 256u * chalf;
       dma4(mp, loff4, g + 4096 + 256 * chalf);
     }
+  };
+  auto issue = [&](int step, int stage, int32_t d) {
+    issue_x(step, stage);
+    issue_w(step, stage, d);
   };
 
   // ---- compute role: W rows 128 wn .. +127 (groups 2 wn, 2 wn + 1), X rows BM/4 wm .. +BM/4-1
@@ -555,6 +562,24 @@ __device__ __forceinline__ void tiled_block(const gemm_problem& P, int local) {
       dn0 = __builtin_amdgcn_ballot_w64((v0 & 1) == PATCH_TILE_DENSE);
       dn1 = __builtin_amdgcn_ballot_w64((v1 & 1) == PATCH_TILE_DENSE);
     }
+  };
+  // Step 0: the three descriptor windows (copies and both compute groups) are
+  // loaded together and step 0's X copies issued behind them, so that their
+  // latencies overlap; the first use of a window waits for all of it (the
+  // compiler does not count the copies, so it waits for them too), then the W
+  // copies follow.  Loaded one after the other, the windows cost two more
+  // memory round trips before the first copy.
+  auto prologue = [&]() {
+    cwin = gwin = 0;
+    gd = g_ok ? desc_window(tile_desc, g_desc, tiles_k, 0, lane) : 0;
+    const int32_t v0 = hok0 ? desc_window(tile_desc, hdesc0, tiles_k, 0, lane) : 1;
+    const int32_t v1 = hok1 ? desc_window(tile_desc, hdesc1, tiles_k, 0, lane) : 1;
+    issue_x(0, 0);
+    dn0 = __builtin_amdgcn_ballot_w64((v0 & 1) == PATCH_TILE_DENSE);
+    dn1 = __builtin_amdgcn_ballot_w64((v1 & 1) == PATCH_TILE_DENSE);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("" : "+v"(gd));
+    issue_w(0, 0, __builtin_amdgcn_readlane(gd, 0));
   };
   auto load_ops = [&](int step, int stage) {
     const uint8_t* cur = lds + stage * STAGE_BYTES;
@@ -619,13 +644,8 @@ __device__ __forceinline__ void tiled_block(const gemm_problem& P, int local) {
   // that every wave finished reading before the barrier.
   // 64-row blocks run two workgroups per CU (128 VGPRs): both wave groups keep
   // the same order there, and the other workgroup on the CU fills the gaps.
-  // The first descriptor windows are loaded before any copy is in flight (a
-  // wait for them would otherwise also wait for the copies).
   constexpr bool LAG = BM > 64;
-  if (nsteps > 0) {
-    compute_window(0);
-    issue(0, 0, copy_desc(0));
-  }
+  if (nsteps > 0) prologue();
   if (!LAG || wn == 0) {
     for (int i = 0; i < nsteps; ++i) {
       const int32_t dnext = i + 1 < nsteps ? copy_desc(i + 1) : 0;
