@@ -16,20 +16,23 @@ using namespace patch_layout;
 
 namespace {
 
-thread_local std::string g_err;
+// The calling thread's last error text: a fixed buffer, so that reporting an
+// error allocates nothing (patch_pack_noalloc promises no host allocation).
+constexpr size_t ERR_BYTES = 512;
+thread_local char g_err[ERR_BYTES];
 
 patch_status fail(patch_status st, const char* fmt, ...) {
-  char buf[512];
+  char buf[ERR_BYTES];  // formatted apart from g_err: an argument may point into it
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
-  g_err = buf;
+  memcpy(g_err, buf, sizeof(buf));
   return st;
 }
 
 patch_status ok() {
-  g_err.clear();
+  g_err[0] = 0;
   return PATCH_OK;
 }
 
@@ -177,7 +180,7 @@ double row_cost(const patch_weight* w, int64_t r0, int64_t r1) {
 
 extern "C" {
 
-const char* patch_last_error(void) { return g_err.c_str(); }
+const char* patch_last_error(void) { return g_err; }
 
 patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, const uint8_t* mask_bits,
                         patch_bit_order order, int32_t tile_n, int32_t tile_k, void* stream, patch_weight** out,
@@ -360,8 +363,7 @@ static patch_status gemm_group_common(const patch_gemm_item* items, int32_t coun
     const patch_status st = check_product(it.w, it.x, it.m, it.ldx, it.y, it.ldy, &skip[i]);
     if (st != PATCH_OK) {
       if (count == 1) return st;
-      const std::string msg = g_err;  // fail() rewrites g_err
-      return fail(st, "product %d: %s", i, msg.c_str());
+      return fail(st, "product %d: %s", i, g_err);  // fail() formats before it rewrites g_err
     }
     if (kernel == PATCH_KERNEL_STREAM && it.m > 16)
       return fail(PATCH_E_INVALID_ARG, "the streaming kernel takes m <= 16, got %lld", (long long)it.m);
