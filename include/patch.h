@@ -2,9 +2,9 @@
  * patch.h -- C ABI of libpatch.so: the PATCH hybrid dense / 2:4 tile GEMM on
  * AMD Instinct MI355X (gfx950).
  *
- * PATCH assigns every tile of a weight matrix to be either dense (0% sparsity)
- * or 2:4 sparse (50%), so the global sparsity can sit anywhere between 0% and
- * 50% ("PATCH: Learnable Tile-level Hybrid Sparsity for LLMs", Abstract).  The
+ * In PATCH each tile of a weight matrix keeps all its weights or is pruned 2:4
+ * (half of them), so the matrix's sparsity can take any value from 0% to 50%
+ * ("PATCH: Learnable Tile-level Hybrid Sparsity for LLMs", Abstract).  The
  * released artifact is a bit-packed binary keep/prune mask over frozen base
  * weights, and applying it zeroes the pruned weights (model card
  * "llama_3.2_1b-PATCH-45Sparse", description and "How to use").  Hardware tiles
