@@ -284,14 +284,16 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
 //
 // Per 256 x 256 step a CU copies 50 KiB (2:4) to 64 KiB (dense) into LDS,
 // its waves read 136 to 192 KiB back, and each SIMD runs 64 (2:4) to 128
-// (dense) smfmacs.  Measured on MI355X: the global -> LDS copies run at 40-48
-// bytes per clock per CU while they are issued, and a wave whose copy finds
-// the fill queue full stops issuing anything; LDS operand reads run at 128
-// bytes per clock with one reading wave per SIMD and about 165 with two; an
-// smfmac takes 17-19 clocks.  So a 90% 2:4 step needs about 1 150 clocks of
-// copy issue, 850 of LDS reads and 1 380 of matrix work per SIMD, and the
-// schedule decides how much of that overlaps (in-kernel timestamps: about
-// 2 650 clocks per step at 256 rows).
+// (dense) smfmacs.  Measured on MI355X: the global -> LDS copies move 40-48
+// bytes per clock per CU while they are issued, without ever filling the
+// fill-path FIFOs (hardware counters), so a copy phase is set by the copy
+// instructions and the scalar instructions around them (M0 writes, address
+// arithmetic; scalar issue takes about 16% of the waves' cycles); LDS operand
+// reads run at 128 bytes per clock with one reading wave per SIMD and about
+// 165 with two; an smfmac takes 17-19 clocks.  So a 90% 2:4 step needs about
+// 1 150 clocks of copy issue, 850 of LDS reads and 1 380 of matrix work per
+// SIMD, and the schedule decides how much of that overlaps (in-kernel
+// timestamps: about 2 550-2 650 clocks per step at 256 rows).
 //
 // LDS holds two stages of BM * 128 + 32 KiB:
 //   X  BM rows x 128 B; 16-byte chunk c of row r at position c ^ (r & 7), so
@@ -308,15 +310,14 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
 // waves of a SIMD run half a step apart: waves 0-3 copy, read and multiply
 // step i; waves 4-7 multiply step i - 1 (read at the end of the previous
 // step), then copy and read step i, so that one wave of each SIMD keeps the
-// matrix unit busy while the other stalls on copy issue or LDS reads.  Against
+// matrix unit busy while the other issues copies or waits for LDS reads.  Against
 // four dedicated copy waves that copy the whole step before multiplying their
 // own share this is 2-5% faster on the 256-row products (timestamps: the copy
 // waves spent about 1 000 clocks issuing before their first smfmac).  Measured
 // and dropped: the lagging waves copying before they multiply (13% slower:
-// both waves of a SIMD stall on the fill path at once), copies interleaved
-// between the smfmacs (35-40% slower: a stalled copy holds back the smfmacs
-// behind it), and three X stages with X copied two steps ahead (160 KiB of
-// LDS, 9% slower).  The copies are issued from inline assembly: the compiler
+// both waves of a SIMD are then busy with copies at once), copies interleaved
+// between the smfmacs (35-40% slower), and three X stages with X copied two
+// steps ahead (160 KiB of LDS, 9% slower).  The copies are issued from inline assembly: the compiler
 // cannot tell that they target the other stage, and as builtins every LDS read
 // after them would wait for them to land.  The two 1 KiB value blocks of a 2:4
 // group share one write of M0 (the LDS address register) through the
@@ -704,9 +705,9 @@ __global__ __launch_bounds__(512, BM == 64 ? 4 : 1) void k_gemm_tiled(const gemm
 // gives each CU at most one workgroup: 12 waves.  Waves 0-7 compute exactly as
 // in k_gemm_tiled (2 x 4 grid, 128 W rows x BM/4 X rows each, two per SIMD);
 // waves 8-11 (one per SIMD) only copy, two steps ahead through three LDS
-// stages (48 KiB each at 128 rows, 40 at 64).  A wave that issues copies
-// stalls while the per-CU fill path drains; here no computing wave ever does,
-// and the third stage hides the copies' latency.  A copy wave writes M0 once
+// stages (48 KiB each at 128 rows, 40 at 64).  Issuing copies takes a wave
+// hundreds of clocks per step; here no computing wave ever does, and the third
+// stage hides the copies' latency.  A copy wave writes M0 once
 // per run of consecutive 1 KiB pool blocks (immediate offsets for the rest), so
 // it issues its copies with fewer scalar instructions: 6-16% faster on the
 // 512 x 2048 products at M = 4096, 1-2% on the 2048-wide ones.
