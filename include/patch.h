@@ -13,8 +13,11 @@
  *
  * This library takes W (bf16, nn.Linear layout [N][K]) plus such a mask,
  * validates that every tile is dense or 2:4 along K, compresses W into a packed
- * weight, and computes Y = X . W_masked^T with dense tiles on bf16 MFMA and 2:4
- * tiles on the sparse MFMA (smfmac) units.
+ * weight, and computes Y = X . W_masked^T on the matrix cores: 2:4 tiles on the
+ * sparse MFMA instruction (smfmac 16x16x64, bf16), dense tiles on the same
+ * instruction twice per 64-wide K step with fixed index words (kept positions
+ * 0, 1 and then 2, 3 of every group of four), which does the dense bf16 MFMA's
+ * work per instruction at its rate.
  *
  * Conventions for every call:
  *   - Pointers marked "device" are HIP device pointers on the current device;
@@ -130,8 +133,9 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
  * patch_gemm -- Y = X . W_masked^T, the linear layer over the packed weight.
  *
  * Y[m][n] = sum_k X[m][k] * Wm[n][k] with bf16 inputs and fp32 accumulation;
- * Wm is W with the pruned weights zeroed (card "How to use").  Dense tiles run
- * on bf16 MFMA, 2:4 tiles on smfmac, so only kept weights are multiplied.
+ * Wm is W with the pruned weights zeroed (card "How to use").  2:4 tiles run
+ * on smfmac with their stored indices, dense tiles on smfmac twice with fixed
+ * indices (dense bf16 MFMA work and rate), so only kept weights are multiplied.
  *
  *   x      device, bf16 [m][ldx], k <= ldx <= PATCH_MAX_LDX, ldx % 8 == 0.
  *   m      >= 0 rows of X (0 is a no-op).
