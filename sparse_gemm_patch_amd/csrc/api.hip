@@ -116,9 +116,9 @@ patch_status check_tile(int64_t n, int64_t k, int32_t tn, int32_t tk) {
   if (n % tn || k % tk)
     return fail(PATCH_E_SHAPE, "W %lldx%lld is not a whole number of %dx%d tiles", (long long)n, (long long)k, tn,
                 tk);
-  if ((n / tn) * (k / tk) > 0x3FFFFFFF) return fail(PATCH_E_SHAPE, "too many tiles");
-  // the GEMM kernels address the packed pools with 32-bit byte offsets
-  if (n * k > PATCH_MAX_WEIGHTS)
+  // the GEMM kernels address the packed pools with 32-bit byte offsets; the
+  // product is tested by division, so that no shape can overflow it
+  if (n > 0 && k > PATCH_MAX_WEIGHTS / n)
     return fail(PATCH_E_SHAPE, "W %lldx%lld has more than 2^31 - 1 weights", (long long)n, (long long)k);
   return PATCH_OK;
 }

@@ -83,6 +83,14 @@ def test_pack_argument_errors(lib):
     assert st == 1                                        # out == NULL
 
 
+@pytest.mark.parametrize("n,k", [(1 << 40, 1 << 40), (1 << 62, 128), (128, 1 << 62), (46400, 46336)])
+def test_pack_rejects_shapes_past_the_weight_limit(lib, n, k):
+    """Shapes whose weight count exceeds 2^31 - 1, including ones where N * K itself would
+    overflow 64 bits, are rejected as PATCH_E_SHAPE before any HIP call."""
+    assert _pack(lib, n=n, k=k, ldw=k) == (2, None)
+    assert b"2^31" in lib.patch_last_error()
+
+
 def test_error_text_names_the_problem(lib):
     _pack(lib, tn=32)
     assert b"64 or 128" in lib.patch_last_error()
