@@ -69,12 +69,18 @@ typedef enum { PATCH_OUT_BF16 = 0, PATCH_OUT_F32 = 1 } patch_out_dtype;
 
 typedef enum { PATCH_TILE_DENSE = 0, PATCH_TILE_SPARSE24 = 1 } patch_tile_type;
 
+/* Largest M the STREAM kernel takes. */
+#define PATCH_STREAM_MAX_M 128
+
 /* Kernel selection for patch_gemm_kernel.  AUTO picks STREAM for M <= 16 and
- * TILED otherwise; forcing one is for tests and measurements. */
+ * TILED for M > PATCH_STREAM_MAX_M; in between it estimates both kernels' time
+ * from the weight's shape and packed bytes and picks STREAM only if it is
+ * estimated at least 10% faster.  Forcing one is for tests and measurements. */
 typedef enum {
   PATCH_KERNEL_AUTO = 0,
   PATCH_KERNEL_TILED = 1,  /* LDS-staged MFMA tiles, for prefill-sized M */
-  PATCH_KERNEL_STREAM = 2  /* weight streaming, one workgroup per 16 rows of W, for M <= 16 (decode) */
+  PATCH_KERNEL_STREAM = 2  /* weight streaming, one workgroup per 16 rows of W, each W chunk applied
+                              to all M rows: decode and batches up to PATCH_STREAM_MAX_M rows */
 } patch_kernel;
 
 typedef struct patch_weight patch_weight; /* opaque, owned by the library */
@@ -153,7 +159,7 @@ patch_status patch_gemm(const patch_weight* w, const uint16_t* x, int64_t m, int
  * `variant` <= 0 lets the library choose; for PATCH_KERNEL_TILED a positive
  * value forces the X rows per workgroup, 256, 192, 128 or 64 (other values:
  * PATCH_E_INVALID_ARG).  It is ignored by PATCH_KERNEL_STREAM and
- * PATCH_KERNEL_AUTO.  PATCH_KERNEL_STREAM needs m <= 16. */
+ * PATCH_KERNEL_AUTO.  PATCH_KERNEL_STREAM needs m <= PATCH_STREAM_MAX_M. */
 patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx,
                                void* y, int64_t ldy, patch_out_dtype y_dtype,
                                patch_kernel kernel, int32_t variant, void* stream);
@@ -164,8 +170,9 @@ patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t
  * A transformer layer applies several linears to the same or to different
  * inputs (the card's model is LLaMA-3.2-1B: q, k, v, o, gate, up and down
  * projections per layer, each with its own PATCH mask).  Each item is the
- * patch_gemm of its own handle, X and Y.  Items with m <= 16 share one launch
- * of the STREAM kernel; TILED items that fill the GPU on their own (at least
+ * patch_gemm of its own handle, X and Y.  Items that run on the STREAM kernel
+ * (as their solo patch_gemm would) share one launch of it (items with m > 64
+ * one launch of their own); TILED items that fill the GPU on their own (at least
  * one 256 x 256 output block per compute unit) get a launch each, and the
  * other TILED items share one launch, so small projections share the chip
  * instead of running one after another; an item with K = 0 gets a zero fill.

@@ -317,6 +317,32 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
   return ok();
 }
 
+// Whether the streaming kernel should run a product of m rows on w.  Decode
+// (m <= 16) always streams.  Up to PATCH_STREAM_MAX_M rows both kernels can,
+// and their estimated times decide.  Streaming: about 3 us, plus the packed W
+// at 5.5 TB/s, plus the X copies (every 16-row block of W copies all m x K of
+// X, rounded up to its 16-row X blocks) at 25 TB/s.  Tiled: these m give it a
+// few 64-row blocks per 128 W rows, so its time is about 4 us plus 0.25 us per
+// 64-wide K step, per round of 256 workgroups.  The tiled kernel keeps a
+// product unless streaming is estimated 10% faster.  Fitted on MI355X to the
+// LLaMA-2-7B 4096 x 4096, 11008 x 4096 and 4096 x 11008 products at m = 16 ..
+// 128 (90% 2:4 tiles); against timings with the weights read from HBM of nine
+// products from 2048 x 2048 to 13824 x 5120 at m = 17 .. 128, the choice was
+// the faster kernel, or within 5% of it, in 53 of 54 cases.
+static bool stream_wins(const patch_weight* w, int64_t m) {
+  if (m <= 16) return true;
+  const int xb = stream_x_blocks(m);
+  if (xb == 0) return false;
+  const double tile = (double)w->tn * (double)w->tk;
+  const double w_bytes = tile * (2.0 * (double)w->n_dense + 1.125 * (double)w->n_sparse);
+  const double x_bytes = (double)(w->n / 16) * 16.0 * xb * (double)w->k * 2.0;
+  const double t_stream = 3.0 + w_bytes / 5.5e6 + x_bytes / 25e6;
+  const double wgs = (double)(w->n / 128) * (double)((m + 63) / 64);
+  const double rounds = wgs > 256 ? (double)(int64_t)((wgs + 255) / 256) : 1.0;
+  const double t_tiled = 4.0 + 0.25 * (double)(w->k / 64) * rounds;
+  return t_stream < 0.9 * t_tiled;
+}
+
 // Checks one product's arguments; sets *skip when it has nothing to compute
 // (m = 0 or n = 0).
 static patch_status check_product(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y,
@@ -365,8 +391,13 @@ static patch_status gemm_group_common(const patch_gemm_item* items, int32_t coun
       if (count == 1) return st;
       return fail(st, "product %d: %s", i, g_err);  // fail() formats before it rewrites g_err
     }
-    if (kernel == PATCH_KERNEL_STREAM && it.m > 16)
-      return fail(PATCH_E_INVALID_ARG, "the streaming kernel takes m <= 16, got %lld", (long long)it.m);
+    if (kernel == PATCH_KERNEL_STREAM && it.m > PATCH_STREAM_MAX_M) {
+      if (count == 1)
+        return fail(PATCH_E_INVALID_ARG, "the streaming kernel takes m <= %d, got %lld", PATCH_STREAM_MAX_M,
+                    (long long)it.m);
+      return fail(PATCH_E_INVALID_ARG, "product %d: the streaming kernel takes m <= %d, got %lld", i,
+                  PATCH_STREAM_MAX_M, (long long)it.m);
+    }
   }
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
@@ -386,7 +417,7 @@ static patch_status gemm_group_common(const patch_gemm_item* items, int32_t coun
       if (e != hipSuccess) return hip_fail(e, "zero-fill launch");
       continue;
     }
-    const bool st = kernel == PATCH_KERNEL_STREAM || (kernel == PATCH_KERNEL_AUTO && it.m <= 16);
+    const bool st = kernel == PATCH_KERNEL_STREAM || (kernel == PATCH_KERNEL_AUTO && stream_wins(it.w, it.m));
     gemm_group& g = st ? streamed : tiled;
     g.p[g.count++] = make_problem(it.w, it.x, it.m, it.ldx, it.y, it.ldy);
   }

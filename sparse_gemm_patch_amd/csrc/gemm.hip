@@ -106,18 +106,20 @@ __device__ __forceinline__ void dma4_at(const void* base, uint32_t off) {
   asm volatile("global_load_lds_dword %0, %1 offset:%2" : : "v"(off), "s"(base), "i"(IMM) : "memory", "m0");
 }
 // ------------------------------------------------------------------------
-// Streaming kernel for M <= 16 (decode).
+// Streaming kernel for small M (decode, and batches up to 16 MB rows).
 //
 // The weight is read once, so this kernel is bound by HBM bandwidth.  One
-// workgroup of 16 waves per 16-row block of W (grid N / 16): the waves take
-// every 16th 64-wide K chunk, each keeping a 16 x 16 accumulator block of
-// Y^T, and are summed through LDS in a fixed order.  No workgroup depends on
-// another (a cross-workgroup reduction would need device-scope fences, which
-// write back a whole XCD's L2 on this chip).  Per chunk a wave loads its A
-// operand (1 KiB of 2:4 values or 2 KiB of dense positions, contiguous, with
-// non-temporal loads) and copies the 16 X rows into its own LDS slot (two
-// global_load_lds copies of 8 rows x 128 bytes; rows past M repeat row M - 1),
-// BATCH chunks at a time.
+// workgroup of WAVES waves per 16-row block of W (grid N / 16): the waves take
+// every WAVES-th 64-wide K chunk, each keeping MB 16 x 16 accumulator blocks
+// of Y^T (one per 16 rows of X), and are summed through LDS in a fixed order.
+// No workgroup depends on another (a cross-workgroup reduction would need
+// device-scope fences, which write back a whole XCD's L2 on this chip).  Per
+// chunk a wave loads its A operand once (1 KiB of 2:4 values or 2 KiB of
+// dense positions, contiguous, with non-temporal loads) and copies the MB x 16
+// X rows into its own LDS slot (two global_load_lds copies of 8 rows x 128
+// bytes per X block; rows past M repeat row M - 1), BATCH chunks at a time;
+// the A operand then meets every X block.  MB = 1 is the decode instance
+// (M <= 16).
 // ------------------------------------------------------------------------
 namespace streamk {
 constexpr int WAVES = 16;
@@ -137,10 +139,10 @@ __device__ __forceinline__ int find_problem(const gemm_group& g, int bid, int& l
   return -1;
 }
 
-template <bool F32>
-__global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
-  using streamk::WAVES;
-  using streamk::BATCH;
+template <bool F32, int MB, int NBLK, int WAVES, int BATCH>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_stream(const gemm_group g) {
+  static_assert(MB >= 1 && MB <= 8, "X blocks per wave");
+  static_assert(NBLK == 1 || NBLK == 2 || NBLK == 4, "16-row W blocks per workgroup");
   int local;
   const int pi = find_problem(g, blockIdx.x, local);
   if (pi < 0) return;
@@ -156,111 +158,139 @@ __global__ __launch_bounds__(1024) void k_gemm_stream(const gemm_group g) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4, r16 = lane & 15;
-  // Blocks in XCD-contiguous order (workgroup i runs on XCD i % 8 and each
-  // product starts on a multiple of 8): the four 16-row blocks that share a
-  // 512-byte group of 2:4 codes run on one XCD and read the codes from its L2
-  // once; dealt round-robin, every XCD fetched them from memory.
+  // Blocks of 16 NBLK W rows in XCD-contiguous order (workgroup i runs on XCD
+  // i % 8 and each product starts on a multiple of 8): the 16-row blocks that
+  // share a 512-byte group of 2:4 codes run on one XCD and read the codes from
+  // its L2 once; dealt round-robin, every XCD fetched them from memory.  A
+  // block's NBLK 16-row blocks lie in one tile (16 NBLK divides TN), so they
+  // share each chunk's tile descriptor and code group.
   const int nb = P.blocks, xcd = local & 7, base_b = nb >> 3, rem_b = nb & 7;
-  const int64_t n0 = (int64_t)(xcd * base_b + (xcd < rem_b ? xcd : rem_b) + (local >> 3)) * 16;
+  const int64_t n0 = (int64_t)(xcd * base_b + (xcd < rem_b ? xcd : rem_b) + (local >> 3)) * (16 * NBLK);
   const int64_t chunks = k >> 6;
   const int ks = tk == 128;                      // 64-wide K chunks per tile column: 1 << ks
   const int ns = tn == 128 ? 7 : 6;              // log2(TN)
   const int64_t desc_row = (n0 >> ns) * tiles_k;
-  const int blk = (int)((n0 & (tn - 1)) >> 4);   // this block's 16-row block inside its tile
+  const int blk = (int)((n0 & (tn - 1)) >> 4);   // first 16-row block of this block inside its tile
   const int bt = tn >> 4;
 
-  // X goes through LDS: per chunk two copies of 8 rows x 128 bytes (whole
-  // lines), 16-byte chunk c of row r at position c ^ (r & 7), into this wave's
-  // slot of the batch; rows past M repeat row M - 1 (they only feed Y rows that
-  // are never stored).  Read straight into the B operand, every load touched
-  // 16 rows x 64 bytes.
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[WAVES * BATCH * 2048];
-  const uint32_t slot0 = (uint32_t)(uintptr_t)smem + (uint32_t)(wave * BATCH * 2048);
-  uint32_t xoff[2];
+  // X goes through LDS: per chunk and X block two copies of 8 rows x 128
+  // bytes (whole lines), 16-byte chunk c of row r at position c ^ (r & 7),
+  // into this wave's slot of the batch; rows past M repeat row M - 1 (they
+  // only feed Y rows that are never stored).  Read straight into the B
+  // operand, every load touched 16 rows x 64 bytes.
+  constexpr int SLOT = MB * 2048;  // one chunk's X blocks
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[WAVES * BATCH * SLOT];
+  const uint32_t slot0 = (uint32_t)(uintptr_t)smem + (uint32_t)(wave * BATCH * SLOT);
+  uint32_t xoff[MB][2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = 8 * h + (lane >> 3);
-    const int64_t rc = row < m ? row : m - 1;
-    xoff[h] = (uint32_t)((rc * ldx + 8 * ((lane & 7) ^ (row & 7))) * 2);
-  }
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 16 * mb + 8 * h + (lane >> 3);
+      const int64_t rc = row < m ? row : m - 1;
+      xoff[mb][h] = (uint32_t)((rc * ldx + 8 * ((lane & 7) ^ (row & 7))) * 2);
+    }
   const uint8_t* dbase = reinterpret_cast<const uint8_t*>(dense_vals) + lane * 16;
   const uint8_t* sbase = reinterpret_cast<const uint8_t*>(sparse_vals) + lane * 16;
   const uint8_t* mbase = sparse_meta + lane * 8;
 
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  // This wave's chunks are c = wave + 16 j.  Their tile descriptors arrive
-  // with one load (lane j holds chunk j's), so that the operand loads of four
-  // chunks can be issued back to back before their MFMAs.
+  f32x4 acc[NBLK][MB];
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[b][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // This wave's chunks are c = wave + WAVES j.  Their tile descriptors arrive
+  // with one load (lane j holds chunk j's), so that the operand loads of a
+  // batch of chunks can be issued back to back before their MFMAs.
   for (int64_t base = wave; base < chunks; base += (int64_t)WAVES * 64) {
     const int nj = (int)min((int64_t)64, (chunks - base + WAVES - 1) / WAVES);
     const int64_t cl = base + (int64_t)WAVES * lane;
     const int32_t dl = lane < nj ? tile_desc[desc_row + (cl >> ks)] : 0;
     for (int j = 0; j < nj; j += BATCH) {
       // BATCH chunks, past the last one clamped to it (loaded, not used): every
-      // chunk issues the same four 16-byte loads whatever its tile type, so
-      // the waits the compiler places stay exact.
+      // chunk issues the same loads whatever its tile type, so the waits the
+      // compiler places stay exact.
       int32_t d[BATCH];
 #pragma unroll
       for (int t = 0; t < BATCH; ++t) d[t] = __builtin_amdgcn_readlane(dl, min(j + t, nj - 1));
-      bf16x16 xb[BATCH];
-      bf16x8 a0[BATCH];
-      u32x4 w2[BATCH];
+      bf16x8 a0[BATCH][NBLK];
+      u32x4 w2[BATCH][NBLK];
 #pragma unroll
       for (int t = 0; t < BATCH; ++t) {
         const int64_t c = base + (int64_t)WAVES * min(j + t, nj - 1);
         const uint16_t* xc = x + (c << 6);
-        dma16(xc, xoff[0], slot0 + t * 2048);
-        dma16(xc, xoff[1], slot0 + t * 2048 + 1024);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          dma16(xc, xoff[mb][0], slot0 + t * SLOT + mb * 2048);
+          dma16(xc, xoff[mb][1], slot0 + t * SLOT + mb * 2048 + 1024);
+        }
         const int64_t slot = d[t] >> 1;
-        const int64_t u = (c & ks) * bt + blk;  // operand unit of this block and chunk
+        const int64_t u = (c & ks) * bt + blk;  // operand unit of the first 16-row block and this chunk
         const bool dn = (d[t] & 1) == PATCH_TILE_DENSE;
         const uint8_t* dw = dbase + (slot * tn * tk + u * 1024) * 2;
         const uint8_t* sw = sbase + slot * tn * tk + u * 1024;
-        const uint8_t* cw = mbase + slot * tn * (tk >> 3) + (u >> 2) * 512;  // lane's 8 bytes of codes
+        const uint8_t* cw = mbase + slot * tn * (tk >> 3) + (u >> 2) * 512;  // lane's 8 bytes of codes (all NBLK blocks)
         // W is read once: non-temporal loads keep it from displacing X in the caches
-        a0[t] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dn ? dw : sw)));
-        w2[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dn ? dw + 1024 : cw));  // dense (2,3), or codes
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) {
+          a0[t][b] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                                                    reinterpret_cast<const u32x4*>(dn ? dw + 2048 * b : sw + 1024 * b)));
+          w2[t][b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dn ? dw + 2048 * b + 1024 : cw));
+        }
       }
       // the X copies are not loads the compiler knows of: wait for them here
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
       for (int t = 0; t < BATCH; ++t) {
-        const uint8_t* sl = smem + (wave * BATCH + t) * 2048 + r16 * 128;
-        xb[t] = cat16(lds8(sl + ((q ^ (r16 & 7)) << 4)), lds8(sl + (((4 + q) ^ (r16 & 7)) << 4)));
-      }
-#pragma unroll
-      for (int t = 0; t < BATCH; ++t) {
         if (j + t >= nj) continue;
         const int64_t c = base + (int64_t)WAVES * (j + t);
-        const int ub = (int)(((c & ks) * bt + blk) & 3);  // block within its 4-block code group
-        if ((d[t] & 1) == PATCH_TILE_DENSE) {
-          acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[t], xb[t], acc, 0x4444, 0, 0);
-          acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, w2[t]), xb[t], acc, 0xEEEE, 0, 0);
-        } else {
-          const uint32_t word = ub < 2 ? w2[t].x : w2[t].y;  // codes of blocks (0,1) or (2,3)
-          acc = ub & 1 ? __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[t], xb[t], acc, (int)word, 0, 1)
-                       : __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[t], xb[t], acc, (int)word, 0, 0);
+        const int u0 = (int)((c & ks) * bt + blk);
+        const bool dn = (d[t] & 1) == PATCH_TILE_DENSE;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const uint8_t* sl = smem + (wave * BATCH + t) * SLOT + mb * 2048 + r16 * 128;
+          const bf16x16 xb = cat16(lds8(sl + ((q ^ (r16 & 7)) << 4)), lds8(sl + (((4 + q) ^ (r16 & 7)) << 4)));
+#pragma unroll
+          for (int b = 0; b < NBLK; ++b) {
+            const int ub = (u0 + b) & 3;  // block within its 4-block code group
+            const uint32_t word = ub < 2 ? w2[t][0].x : w2[t][0].y;  // codes of blocks (0,1) or (2,3)
+            if (dn) {
+              acc[b][mb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[t][b], xb, acc[b][mb], 0x4444, 0, 0);
+              acc[b][mb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, w2[t][b]), xb,
+                                                                     acc[b][mb], 0xEEEE, 0, 0);
+            } else {
+              acc[b][mb] = ub & 1 ? __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[t][b], xb, acc[b][mb], (int)word, 0, 1)
+                                  : __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a0[t][b], xb, acc[b][mb], (int)word, 0, 0);
+            }
+          }
         }
       }
     }
   }
 
-  // Sum the waves in a fixed order: lane holds rows 4 q + i of column m = r16.
-  // The X slots are free once every wave is past its last chunk.
-  static_assert(WAVES * 16 * 17 * 4 <= WAVES * BATCH * 2048, "reduction fits the X slots");
-  float(*red)[16][17] = reinterpret_cast<float(*)[16][17]>(smem);
-  __syncthreads();
+  // Sum the waves in a fixed order, one 16-row W block at a time: lane holds
+  // rows 4 q + i of column m = r16 of each X block.  The X slots are free once
+  // every wave is past its last chunk.
+  static_assert(WAVES * MB * 16 * 17 * 4 <= WAVES * BATCH * SLOT, "reduction fits the X slots");
+  float(*red)[MB][16][17] = reinterpret_cast<float(*)[MB][16][17]>(smem);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][4 * q + i][r16] = acc[i];
-  __syncthreads();
-  if (threadIdx.x < 256) {
-    const int nl = threadIdx.x >> 4, mm = threadIdx.x & 15;
-    float v = 0.f;
+  for (int b = 0; b < NBLK; ++b) {
+    __syncthreads();
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) v += red[w][nl][mm];
-    if (mm < m) {
-      if (F32) reinterpret_cast<float*>(y)[mm * ldy + n0 + nl] = v;
-      else reinterpret_cast<uint16_t*>(y)[mm * ldy + n0 + nl] = f32_to_bf16_rne(v);
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][mb][4 * q + i][r16] = acc[b][mb][i];
+    __syncthreads();
+    for (int o = threadIdx.x; o < 256 * MB; o += 64 * WAVES) {
+      const int mb = o >> 8, nl = (o >> 4) & 15, mm = 16 * mb + (o & 15);
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) v += red[w][mb][nl][o & 15];
+      if (mm < m) {
+        const int64_t col = n0 + 16 * b + nl;
+        if (F32) reinterpret_cast<float*>(y)[mm * ldy + col] = v;
+        else reinterpret_cast<uint16_t*>(y)[mm * ldy + col] = f32_to_bf16_rne(v);
+      }
     }
   }
 }
@@ -1018,19 +1048,73 @@ gemm_problem make_problem(const patch_weight* w, const uint16_t* x, int64_t m, i
   return p;
 }
 
-hipError_t launch_stream_group(gemm_group& g, int out_f32, hipStream_t s) {
+namespace {
+// PATCH_LOG=1 in the environment prints every GEMM launch's plan to stderr:
+// block height, grid and the entries with their W-row ranges.
+bool log_launches() {
+  static const bool on = [] {
+    const char* e = getenv("PATCH_LOG");
+    return e && *e && *e != '0';
+  }();
+  return on;
+}
+
+}  // namespace
+
+namespace {
+template <bool F32, int MB, int NBLK, int WAVES, int BATCH>
+hipError_t launch_stream_mb(gemm_group& g, hipStream_t s) {
   int64_t total = 0;
   for (int i = 0; i < g.count; ++i) {  // each product starts on a multiple of 8 (its XCD order)
     g.p[i].block0 = (int32_t)total;
-    g.p[i].blocks = (int32_t)(g.p[i].n / 16);
+    g.p[i].blocks = (int32_t)(g.p[i].n / (16 * NBLK));
     total += (g.p[i].blocks + 7) / 8 * 8;
   }
   if (total == 0) return hipSuccess;
   if (total > INT32_MAX) return hipErrorInvalidValue;  // block numbers are 32-bit
-  const dim3 block(64 * streamk::WAVES);
-  if (out_f32) hipLaunchKernelGGL(k_gemm_stream<true>, dim3((unsigned)total), block, 0, s, g);
-  else hipLaunchKernelGGL(k_gemm_stream<false>, dim3((unsigned)total), block, 0, s, g);
+  hipLaunchKernelGGL((k_gemm_stream<F32, MB, NBLK, WAVES, BATCH>), dim3((unsigned)total), dim3(64 * WAVES), 0, s, g);
   return hipGetLastError();
+}
+template <bool F32>
+hipError_t launch_stream_f(gemm_group& g, int mb, hipStream_t s) {
+  // LDS per workgroup: WAVES x BATCH x MB x 2 KiB of X slots.  Decode (MB = 1)
+  // keeps two chunks in flight per wave (64 KiB, two workgroups per CU); the
+  // wider instances keep one (64, 128 and 128 KiB); MB = 8 runs 8 waves, whose
+  // 32 accumulators and operands fit 256 registers.
+  switch (mb) {
+    case 1: return launch_stream_mb<F32, 1, 1, streamk::WAVES, streamk::BATCH>(g, s);
+    case 2: return launch_stream_mb<F32, 2, 1, 16, 1>(g, s);
+    case 4: return launch_stream_mb<F32, 4, 1, 16, 1>(g, s);
+    case 8: return launch_stream_mb<F32, 8, 1, 8, 1>(g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace
+
+int stream_x_blocks(int64_t m) { return m <= 16 ? 1 : m <= 32 ? 2 : m <= 64 ? 4 : m <= PATCH_STREAM_MAX_M ? 8 : 0; }
+
+// The instances with 1, 2 and 4 X blocks per wave split K among 16 waves
+// alike, so a product's Y has the same bits whichever of them runs it: a
+// launch sizes its X blocks for its largest m.  The 8-block instance splits K
+// among 8 waves; its products (m > 64) get a launch of their own, so that a
+// product's Y never depends on the others in its group.
+hipError_t launch_stream_group(gemm_group& g, int out_f32, hipStream_t s) {
+  gemm_group part[2] = {};
+  int mb[2] = {1, 8};
+  for (int i = 0; i < g.count; ++i) {
+    const int xb = stream_x_blocks(g.p[i].m);
+    if (xb == 0) return hipErrorInvalidValue;
+    gemm_group& h = part[xb == 8];
+    h.p[h.count++] = g.p[i];
+    if (xb < 8 && xb > mb[0]) mb[0] = xb;
+  }
+  for (int j = 0; j < 2; ++j) {
+    if (part[j].count == 0) continue;
+    if (log_launches()) fprintf(stderr, "patch: k_gemm_stream x_blocks %d products %d\n", mb[j], part[j].count);
+    const hipError_t e = out_f32 ? launch_stream_f<true>(part[j], mb[j], s) : launch_stream_f<false>(part[j], mb[j], s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 namespace {
@@ -1166,16 +1250,6 @@ void plan_tail(gemm_group& g, int G) {
   tail.bm = 192;
   last.n = tail.n_begin;
   g.p[g.count++] = tail;
-}
-
-// PATCH_LOG=1 in the environment prints every tiled launch's plan to stderr:
-// block height, grid and the entries with their W-row ranges.
-bool log_launches() {
-  static const bool on = [] {
-    const char* e = getenv("PATCH_LOG");
-    return e && *e && *e != '0';
-  }();
-  return on;
 }
 
 void log_plan(const char* kernel, const gemm_group& g, int grid) {

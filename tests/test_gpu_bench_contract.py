@@ -17,9 +17,9 @@ TOP = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "h
        "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline")
 
 
-def run_bench(*extra):
-    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1", "--no-sweep",
-           "--no-grouped", "--no-sample", "--no-split", *extra]
+def run_bench(*extra, sweep=False):
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1",
+           *([] if sweep else ["--no-sweep"]), "--no-grouped", "--no-sample", "--no-split", *extra]
     print("bench:", " ".join(cmd[1:]), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -57,10 +57,12 @@ def test_default_workload_line():
 
 
 def test_decode_workload_line():
-    d = run_bench("--workload", "llama7b-decode", "--no-cpu-baseline")
+    d = run_bench("--workload", "llama7b-decode", "--no-cpu-baseline", sweep=True)
     r = check_common(d)
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert d["cpu_baseline"] is None and d["weight_copies"] >= 2
+    assert sorted(d["other_m"]) == ["M=1", "M=128", "M=32", "M=64", "M=8"]
+    assert all(v["dense_eq_tflops"] > 0 for v in d["other_m"].values())
 
 
 @pytest.mark.parametrize("wl", ["llama7b-model-prefill", "llama7b-model-decode"])

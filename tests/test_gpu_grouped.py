@@ -153,8 +153,11 @@ def test_group_errors_launch_nothing(P):
         big[i] = items[0]
     st = lib.patch_gemm_grouped(big, 17, 1, None)
     assert P.STATUS[st] == "PATCH_E_INVALID_ARG"
-    st = lib.patch_gemm_grouped_kernel(items, 2, 1, 2, 0, None)  # forced streaming with m = 24
+    over = (P.GemmItem * 2)(items[0], items[1])
+    over[1].m = 129  # forced streaming past its 128 rows: rejected before any launch
+    st = lib.patch_gemm_grouped_kernel(over, 2, 1, 2, 0, None)
     assert P.STATUS[st] == "PATCH_E_INVALID_ARG"
+    assert "product 1" in lib.patch_last_error().decode()
 
 
 def test_block_rows_do_not_change_bits(P):
@@ -167,3 +170,16 @@ def test_block_rows_do_not_change_bits(P):
     ys = [pw.gemm(x, out_dtype=torch.float32, kernel="tiled", block_m=b) for b in (256, 192, 128, 64)]
     torch.cuda.synchronize()
     assert all(torch.equal(ys[0], y) for y in ys[1:])
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("kernel", ["auto", "stream"])
+def test_group_mixing_stream_batch_sizes(P, kernel, out_dtype):
+    """Streamed items of 4, 40 and 100 rows (1, 4 and 8 blocks of 16 X rows per wave; the last in a
+    launch of its own) beside a tiled one: each equals its solo launch bit for bit."""
+    specs = [(4, 512, 4096, 128, 128, 0.9), (40, 256, 4096, 128, 64, 0.5), (100, 256, 8192, 64, 128, 0.7)]
+    if kernel == "auto":
+        specs.append((300, 512, 512, 128, 128, 0.9))
+    probs = [I.make_problem("mix", m, n, k, tn, tk, frac=f, cfg=71, matrix=i)
+             for i, (m, n, k, tn, tk, f) in enumerate(specs)]
+    run_group(P, probs, out_dtype, kernel=kernel)

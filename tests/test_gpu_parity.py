@@ -222,9 +222,10 @@ def test_ones_count_kept_exactly(P, kernel, m):
 
 
 @pytest.mark.parametrize("k", [64, 192, 1088, 2048, 4160])
-@pytest.mark.parametrize("m", [1, 5, 16])
+@pytest.mark.parametrize("m", [1, 5, 16, 40, 100])
 def test_stream_k_ranges_and_determinism(P, k, m):
-    """16 waves share the K chunks of a block: fewer chunks than waves, a ragged last round, many rounds."""
+    """16 waves (8 with more than 64 rows) share the K chunks of a block: fewer chunks than waves,
+    a ragged last round, many rounds."""
     prob = I.make_problem("sk", m, 512, k, 128, 64, frac=0.5, cfg=42)
     pw = pack_problem(P, prob)
     x = dev_u16(prob.x)
@@ -336,3 +337,65 @@ def test_ldx_limit(P):
     st = lib.patch_gemm(pw._h, x.data_ptr(), 1, (1 << 22) + 8, y.data_ptr(), 128, 0, None)
     assert P.STATUS[st] == "PATCH_E_INVALID_ARG"
     assert b"exceeds" in lib.patch_last_error()
+
+
+@pytest.mark.parametrize("tn,tk", TILES)
+@pytest.mark.parametrize("m", [17, 32, 33, 64, 65, 100, 128])
+def test_stream_batched_matches_oracle(P, tn, tk, m):
+    """The streaming kernel with 2, 4 or 8 blocks of 16 X rows per wave: every tile size, ragged m,
+    all-dense, mixed and all-2:4 weights; bf16 Y is the fp32 Y rounded to nearest even; run to run
+    bitwise."""
+    for frac in (0.0, 0.5, 1.0):
+        prob = I.make_problem("sb", m, 384, 640, tn, tk, frac=frac, cfg=90 + m)
+        pw = pack_problem(P, prob)
+        x = dev_u16(prob.x)
+        y32 = pw.gemm(x, out_dtype=torch.float32, kernel="stream")
+        y32b = pw.gemm(x, out_dtype=torch.float32, kernel="stream")
+        y16 = pw.gemm(x, out_dtype=torch.bfloat16, kernel="stream")
+        torch.cuda.synchronize()
+        ref = O.gemm_ref(prob.x, O.masked_weight(prob.w, prob.mask))
+        assert O.rel_error(y_host(y32), ref) <= 1e-4, frac
+        assert O.rel_error(y_host(y16), ref) <= TOL, frac
+        assert torch.equal(y32, y32b), frac
+        assert torch.equal(y16, y32.to(torch.bfloat16)), frac
+
+
+@pytest.mark.parametrize("m", [32, 64])
+def test_stream_rows_independent_of_batch(P, m):
+    """With 1, 2 and 4 X blocks per wave the waves split K alike, so every 16-row slice of a
+    batched product equals, bit for bit, the product of that slice alone."""
+    prob = I.make_problem("sr", m, 256, 1088, 128, 64, frac=0.6, cfg=95)
+    pw = pack_problem(P, prob)
+    x = dev_u16(prob.x)
+    y = pw.gemm(x, out_dtype=torch.float32, kernel="stream")
+    for r0 in range(0, m, 16):
+        ys = pw.gemm(x[r0:r0 + 16].contiguous(), out_dtype=torch.float32, kernel="stream")
+        torch.cuda.synchronize()
+        assert torch.equal(y[r0:r0 + 16], ys), r0
+
+
+def test_stream_rejects_more_than_128_rows(P):
+    prob = I.make_problem("s129", 129, 128, 128, 64, 64, frac=0.5, cfg=96)
+    pw = pack_problem(P, prob)
+    with pytest.raises(P.PatchError) as e:
+        pw.gemm(dev_u16(prob.x), kernel="stream")
+    assert e.value.status_name == "PATCH_E_INVALID_ARG"
+
+
+@pytest.mark.parametrize("n,k,m,want", [(1024, 8192, 64, "stream"), (16384, 1024, 128, "tiled")])
+def test_auto_kernel_for_small_batches(P, n, k, m, want):
+    """Between 17 and 128 rows AUTO estimates both kernels: a narrow weight with a long K streams
+    (the tiled kernel would give it 8 workgroups of 128 K steps), a wide one with a short K stays
+    tiled (streaming would copy all of X for each of its 1024 row blocks)."""
+    prob = I.make_problem("am", m, n, k, 128, 128, frac=0.9, cfg=97)
+    pw = pack_problem(P, prob)
+    x = dev_u16(prob.x)
+    ya = pw.gemm(x, out_dtype=torch.float32)
+    ys = pw.gemm(x, out_dtype=torch.float32, kernel="stream")
+    yt = pw.gemm(x, out_dtype=torch.float32, kernel="tiled")
+    torch.cuda.synchronize()
+    assert not torch.equal(ys, yt)  # the two kernels sum in different orders: the check can tell them apart
+    assert torch.equal(ya, ys if want == "stream" else yt)
+    rows = np.arange(0, m, 7)
+    ref = O.gemm_ref(prob.x[rows], O.masked_weight(prob.w, prob.mask))
+    assert O.rel_error(y_host(ya)[rows], ref) <= 1e-4
