@@ -5,7 +5,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <new>
 #include <string>
 #include <vector>
@@ -319,28 +321,32 @@ patch_status patch_pack(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, co
 
 // Whether the streaming kernel should run a product of m rows on w.  Decode
 // (m <= 16) always streams.  Up to PATCH_STREAM_MAX_M rows both kernels can,
-// and their estimated times decide.  Streaming: about 3 us, plus the packed W
-// at 5.5 TB/s, plus the X copies (every 16-row block of W copies all m x K of
-// X, rounded up to its 16-row X blocks) at 25 TB/s.  Tiled: these m give it a
-// few 64-row blocks per 128 W rows, so its time is about 4 us plus 0.25 us per
-// 64-wide K step, per round of 256 workgroups.  The tiled kernel keeps a
-// product unless streaming is estimated 10% faster.  Fitted on MI355X to the
-// LLaMA-2-7B 4096 x 4096, 11008 x 4096 and 4096 x 11008 products at m = 16 ..
-// 128 (90% 2:4 tiles); against timings with the weights read from HBM of nine
-// products from 2048 x 2048 to 13824 x 5120 at m = 17 .. 128, the choice was
-// the faster kernel, or within 5% of it, in 53 of 54 cases.
+// and their estimated times (us) decide.  Both launches are bound by latency
+// here, so the estimates count serial steps, with the plain HBM read of the
+// packed W (5.5 TB/s, plus the launch) as a floor.  Streaming: 5.7, plus the X
+// copies (every workgroup copies all of X, rounded up to its 16-row X blocks)
+// at 50 TB/s, plus 0.54 per chunk a wave waits for in turn (one in flight), plus
+// 0.085 per 16 x 16 x 64 block of products a wave issues.  Tiled: these m give
+// it one or two 64-row blocks per 128 W rows, so 5.4 plus 0.285 per 64-wide K
+// step, per round of 256 workgroups.  Fitted on MI355X to timings with the
+// weights read from HBM (90% 2:4 tiles, ten products from 2048 x 8192 to
+// 14336 x 4096, m = 17 .. 128): the choice was the faster kernel in all 52
+// cases.
 static bool stream_wins(const patch_weight* w, int64_t m) {
   if (m <= 16) return true;
   const int xb = stream_x_blocks(m);
   if (xb == 0) return false;
+  const int nblk = stream_w_blocks(w->n), waves = stream_waves(m, w->n);  // one chunk in flight per wave
   const double tile = (double)w->tn * (double)w->tk;
-  const double w_bytes = tile * (2.0 * (double)w->n_dense + 1.125 * (double)w->n_sparse);
-  const double x_bytes = (double)(w->n / 16) * 16.0 * xb * (double)w->k * 2.0;
-  const double t_stream = 3.0 + w_bytes / 5.5e6 + x_bytes / 25e6;
+  const double w_floor = tile * (2.0 * (double)w->n_dense + 1.125 * (double)w->n_sparse) / 5.5e6;
+  const double chunks = (double)(w->k / 64);
+  const double x_bytes = (double)(w->n / (16 * nblk)) * (16.0 * xb) * (double)w->k * 2.0;
+  const double per_wave = std::ceil(chunks / waves);
+  const double t_stream = std::max(5.7 + x_bytes / 50e6 + 0.54 * per_wave + 0.085 * per_wave * xb * nblk, 3.0 + w_floor);
   const double wgs = (double)(w->n / 128) * (double)((m + 63) / 64);
   const double rounds = wgs > 256 ? (double)(int64_t)((wgs + 255) / 256) : 1.0;
-  const double t_tiled = 4.0 + 0.25 * (double)(w->k / 64) * rounds;
-  return t_stream < 0.9 * t_tiled;
+  const double t_tiled = std::max(5.4 + 0.285 * chunks * rounds, 4.0 + w_floor);
+  return t_stream < t_tiled;
 }
 
 // Checks one product's arguments; sets *skip when it has nothing to compute

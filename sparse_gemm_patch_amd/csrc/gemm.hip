@@ -109,19 +109,24 @@ __device__ __forceinline__ void dma4_at(const void* base, uint32_t off) {
 // Streaming kernel for small M (decode, and batches up to 16 MB rows).
 //
 // The weight is read once, so this kernel is bound by HBM bandwidth.  One
-// workgroup of WAVES waves per 16-row block of W (grid N / 16): the waves take
-// every WAVES-th 64-wide K chunk, each keeping MB 16 x 16 accumulator blocks
-// of Y^T (one per 16 rows of X), and are summed through LDS in a fixed order.
-// No workgroup depends on another (a cross-workgroup reduction would need
-// device-scope fences, which write back a whole XCD's L2 on this chip).  Per
-// chunk a wave loads its A operand once (1 KiB of 2:4 values or 2 KiB of
-// dense positions, contiguous, with non-temporal loads) and copies the MB x 16
-// X rows into its own LDS slot (two global_load_lds copies of 8 rows x 128
-// bytes per X block; rows past M repeat row M - 1), BATCH chunks at a time;
-// the A operand then meets every X block.  MB = 1 is the decode instance
-// (M <= 16).
+// workgroup of WAVES waves per NBLK 16-row blocks of W (grid N / (16 NBLK)):
+// the waves take every WAVES-th 64-wide K chunk, each keeping NBLK x MB
+// 16 x 16 accumulator blocks of Y^T (MB = one per 16 rows of X), and are
+// summed through LDS in a fixed order.  No workgroup depends on another (a
+// cross-workgroup reduction would need device-scope fences, which write back
+// a whole XCD's L2 on this chip).  Per chunk a wave loads its A operands once
+// (1 KiB of 2:4 values or 2 KiB of dense positions per W block, contiguous,
+// with non-temporal loads) and copies the MB x 16 X rows into its own LDS
+// slot (two global_load_lds copies of 8 rows x 128 bytes per X block; rows
+// past M repeat row M - 1), BATCH chunks at a time; every A operand then
+// meets every X block.  MB = 1 serves decode (M <= 16).
+//
+// Every workgroup copies all of X, so NBLK divides that traffic and MB
+// multiplies it; NBLK also divides the grid, and a grid of fewer than about
+// 160 workgroups leaves the chip's fetch latency exposed (stream_w_blocks).
 // ------------------------------------------------------------------------
 namespace streamk {
+// the decode instance with one W block per workgroup
 constexpr int WAVES = 16;
 constexpr int BATCH = 2;  // chunks per wave in flight together (1: 7-20% slower; 4: up to 19% slower, one workgroup per CU)
 }  // namespace streamk
@@ -1076,16 +1081,30 @@ hipError_t launch_stream_mb(gemm_group& g, hipStream_t s) {
   return hipGetLastError();
 }
 template <bool F32>
-hipError_t launch_stream_f(gemm_group& g, int mb, hipStream_t s) {
-  // LDS per workgroup: WAVES x BATCH x MB x 2 KiB of X slots.  Decode (MB = 1)
-  // keeps two chunks in flight per wave (64 KiB, two workgroups per CU); the
-  // wider instances keep one (64, 128 and 128 KiB); MB = 8 runs 8 waves, whose
-  // 32 accumulators and operands fit 256 registers.
-  switch (mb) {
-    case 1: return launch_stream_mb<F32, 1, 1, streamk::WAVES, streamk::BATCH>(g, s);
-    case 2: return launch_stream_mb<F32, 2, 1, 16, 1>(g, s);
-    case 4: return launch_stream_mb<F32, 4, 1, 16, 1>(g, s);
-    case 8: return launch_stream_mb<F32, 8, 1, 8, 1>(g, s);
+hipError_t launch_stream_f(gemm_group& g, int waves, int nblk, int mb, hipStream_t s) {
+  // LDS per workgroup: WAVES x BATCH x MB x 2 KiB of X slots.  Decode with one
+  // W block (MB = 1, 16 waves) keeps two chunks in flight per wave (64 KiB, two
+  // workgroups per CU); the other instances keep one.  Eight waves carry the
+  // wider accumulator sets (up to 4 x 8 blocks: 128 registers).
+  if (waves == streamk::WAVES && nblk == 1) {
+    switch (mb) {
+      case 1: return launch_stream_mb<F32, 1, 1, streamk::WAVES, streamk::BATCH>(g, s);
+      case 2: return launch_stream_mb<F32, 2, 1, 16, 1>(g, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (waves != 8) return hipErrorInvalidValue;
+  switch (nblk * 16 + mb) {
+    case 16 + 4: return launch_stream_mb<F32, 4, 1, 8, 1>(g, s);
+    case 16 + 8: return launch_stream_mb<F32, 8, 1, 8, 1>(g, s);
+    case 32 + 1: return launch_stream_mb<F32, 1, 2, 8, 2>(g, s);
+    case 32 + 2: return launch_stream_mb<F32, 2, 2, 8, 1>(g, s);
+    case 32 + 4: return launch_stream_mb<F32, 4, 2, 8, 1>(g, s);
+    case 32 + 8: return launch_stream_mb<F32, 8, 2, 8, 1>(g, s);
+    case 64 + 1: return launch_stream_mb<F32, 1, 4, 8, 1>(g, s);
+    case 64 + 2: return launch_stream_mb<F32, 2, 4, 8, 1>(g, s);
+    case 64 + 4: return launch_stream_mb<F32, 4, 4, 8, 1>(g, s);
+    case 64 + 8: return launch_stream_mb<F32, 8, 4, 8, 1>(g, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1093,25 +1112,47 @@ hipError_t launch_stream_f(gemm_group& g, int mb, hipStream_t s) {
 
 int stream_x_blocks(int64_t m) { return m <= 16 ? 1 : m <= 32 ? 2 : m <= 64 ? 4 : m <= PATCH_STREAM_MAX_M ? 8 : 0; }
 
-// The instances with 1, 2 and 4 X blocks per wave split K among 16 waves
-// alike, so a product's Y has the same bits whichever of them runs it: a
-// launch sizes its X blocks for its largest m.  The 8-block instance splits K
-// among 8 waves; its products (m > 64) get a launch of their own, so that a
-// product's Y never depends on the others in its group.
+// Measured on MI355X with the weights read from HBM (90% 2:4 tiles, N from
+// 2048 to 14336, m from 1 to 128): the fastest W-block count was the largest
+// that still leaves 160 workgroups, e.g. 4 for 11008 and 13824 rows (up to 32%
+// faster than one block at m = 16, 25% at m = 32), 2 for 5120 to 8192, 1 for
+// 4096 and below.
+int stream_w_blocks(int64_t n) { return n >= 160 * 64 ? 4 : n >= 160 * 32 ? 2 : 1; }
+
+// 16 waves split K for one W block and at most two X blocks (4-19% faster
+// than 8 there on long-K products at m = 17); 8 waves otherwise (up to 40%
+// faster than 16 with four W or X blocks: half the reduction, and two
+// workgroups per CU).
+int stream_waves(int64_t m, int64_t n) { return stream_w_blocks(n) == 1 && stream_x_blocks(m) <= 2 ? 16 : 8; }
+
+// A product's Y depends only on how many waves split its K (each wave sums its
+// chunks in order, then the waves are summed in order), not on how many X or W
+// blocks a workgroup carries, and its wave count depends only on its own m and
+// n.  So a launch takes the products of one (waves, W blocks) family and sizes
+// its X blocks for their largest m: a product's Y never depends on the others
+// in its group.
 hipError_t launch_stream_group(gemm_group& g, int out_f32, hipStream_t s) {
-  gemm_group part[2] = {};
-  int mb[2] = {1, 8};
+  // families: 16 waves x 1 W block, 8 waves x 1, 2 or 4 W blocks
+  gemm_group part[4] = {};
+  int mb[4] = {1, 1, 1, 1};
   for (int i = 0; i < g.count; ++i) {
     const int xb = stream_x_blocks(g.p[i].m);
     if (xb == 0) return hipErrorInvalidValue;
-    gemm_group& h = part[xb == 8];
+    const int nblk = stream_w_blocks(g.p[i].n);
+    const int j = stream_waves(g.p[i].m, g.p[i].n) == 16 ? 0 : nblk == 1 ? 1 : nblk == 2 ? 2 : 3;
+    gemm_group& h = part[j];
     h.p[h.count++] = g.p[i];
-    if (xb < 8 && xb > mb[0]) mb[0] = xb;
+    if (xb > mb[j]) mb[j] = xb;
   }
-  for (int j = 0; j < 2; ++j) {
+  static const int waves[4] = {16, 8, 8, 8}, nblks[4] = {1, 1, 2, 4};
+  for (int j = 0; j < 4; ++j) {
     if (part[j].count == 0) continue;
-    if (log_launches()) fprintf(stderr, "patch: k_gemm_stream x_blocks %d products %d\n", mb[j], part[j].count);
-    const hipError_t e = out_f32 ? launch_stream_f<true>(part[j], mb[j], s) : launch_stream_f<false>(part[j], mb[j], s);
+    if (j == 1 && mb[j] < 4) mb[j] = 4;  // one W block with 8 waves: only for m > 32
+    if (log_launches())
+      fprintf(stderr, "patch: k_gemm_stream waves %d w_blocks %d x_blocks %d products %d\n", waves[j], nblks[j], mb[j],
+              part[j].count);
+    const hipError_t e = out_f32 ? launch_stream_f<true>(part[j], waves[j], nblks[j], mb[j], s)
+                                 : launch_stream_f<false>(part[j], waves[j], nblks[j], mb[j], s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -102,6 +102,10 @@ gemm_problem make_problem(const patch_weight* w, const uint16_t* x, int64_t m, i
 // PATCH_STREAM_MAX_M (patch.h): 8 blocks of 16 X rows per wave.
 // 16-row X blocks per wave of the streaming kernel for m rows (0 past PATCH_STREAM_MAX_M).
 int stream_x_blocks(int64_t m);
+// 16-row W blocks per workgroup of the streaming kernel for an n-row W (1, 2 or 4).
+int stream_w_blocks(int64_t n);
+// Waves that split K in the streaming kernel for an m x n product (16 or 8).
+int stream_waves(int64_t m, int64_t n);
 // One launch of the streaming kernel (every m <= PATCH_STREAM_MAX_M) / the
 // tiled kernel over a group.  block_m > 0 forces the tiled block height (256,
 // 192, 128, 64).

@@ -175,11 +175,26 @@ def test_block_rows_do_not_change_bits(P):
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("kernel", ["auto", "stream"])
 def test_group_mixing_stream_batch_sizes(P, kernel, out_dtype):
-    """Streamed items of 4, 40 and 100 rows (1, 4 and 8 blocks of 16 X rows per wave; the last in a
-    launch of its own) beside a tiled one: each equals its solo launch bit for bit."""
+    """Streamed items of 4, 40 and 100 rows (1, 4 and 8 blocks of 16 X rows per wave; the first with
+    16 waves, the others with 8 in a launch of their own) beside a tiled one: each equals its solo
+    launch bit for bit."""
     specs = [(4, 512, 4096, 128, 128, 0.9), (40, 256, 4096, 128, 64, 0.5), (100, 256, 8192, 64, 128, 0.7)]
     if kernel == "auto":
         specs.append((300, 512, 512, 128, 128, 0.9))
     probs = [I.make_problem("mix", m, n, k, tn, tk, frac=f, cfg=71, matrix=i)
              for i, (m, n, k, tn, tk, f) in enumerate(specs)]
     run_group(P, probs, out_dtype, kernel=kernel)
+
+
+@pytest.mark.parametrize("kernel", ["auto", "stream"])
+def test_group_mixing_stream_families(P, kernel):
+    """Streamed items whose wave counts and W blocks per workgroup differ (one W block with 16 or 8
+    waves, 2 and 4 W blocks with 8) run in one launch per family; each equals its solo launch bit
+    for bit and the oracle."""
+    specs = [(8, 10240, 320, 64, 64, 0.9), (40, 5120, 256, 128, 128, 0.5), (20, 1024, 512, 128, 64, 0.7),
+             (100, 10240, 384, 128, 128, 0.3), (50, 512, 384, 64, 128, 1.0), (3, 5120, 128, 64, 64, 0.0),
+             (128, 256, 640, 128, 128, 0.6)]
+    probs = [I.make_problem("fam", m, n, k, tn, tk, frac=f, cfg=72, matrix=i)
+             for i, (m, n, k, tn, tk, f) in enumerate(specs)]
+    run_group(P, probs, torch.float32, kernel=kernel)
+    run_group(P, probs, torch.bfloat16, kernel=kernel)

@@ -224,7 +224,7 @@ def test_ones_count_kept_exactly(P, kernel, m):
 @pytest.mark.parametrize("k", [64, 192, 1088, 2048, 4160])
 @pytest.mark.parametrize("m", [1, 5, 16, 40, 100])
 def test_stream_k_ranges_and_determinism(P, k, m):
-    """16 waves (8 with more than 64 rows) share the K chunks of a block: fewer chunks than waves,
+    """16 waves (8 with more than 32 rows) share the K chunks of a block: fewer chunks than waves,
     a ragged last round, many rounds."""
     prob = I.make_problem("sk", m, 512, k, 128, 64, frac=0.5, cfg=42)
     pw = pack_problem(P, prob)
@@ -360,18 +360,44 @@ def test_stream_batched_matches_oracle(P, tn, tk, m):
         assert torch.equal(y16, y32.to(torch.bfloat16)), frac
 
 
-@pytest.mark.parametrize("m", [32, 64])
-def test_stream_rows_independent_of_batch(P, m):
-    """With 1, 2 and 4 X blocks per wave the waves split K alike, so every 16-row slice of a
-    batched product equals, bit for bit, the product of that slice alone."""
-    prob = I.make_problem("sr", m, 256, 1088, 128, 64, frac=0.6, cfg=95)
+@pytest.mark.parametrize("n,m,rows", [(256, 32, 16), (256, 128, 64), (5120, 128, 16), (10240, 100, 16)])
+def test_stream_rows_independent_of_batch(P, n, m, rows):
+    """A product's Y depends on how many waves split K, not on how many X blocks a wave carries:
+    16 waves for one W block and up to 32 rows, 8 otherwise.  So a slice of a batched product run
+    alone, with the same wave count, equals that slice of the batch bit for bit (256 rows of W: one
+    W block, 16-row slices of 32 rows and 64-row slices of 128; 5120 and 10240 rows: 2 and 4 W
+    blocks, 8 waves for every m)."""
+    prob = I.make_problem("sr", m, n, 1088, 128, 64, frac=0.6, cfg=95)
     pw = pack_problem(P, prob)
     x = dev_u16(prob.x)
     y = pw.gemm(x, out_dtype=torch.float32, kernel="stream")
-    for r0 in range(0, m, 16):
-        ys = pw.gemm(x[r0:r0 + 16].contiguous(), out_dtype=torch.float32, kernel="stream")
+    for r0 in range(0, m, rows):
+        ys = pw.gemm(x[r0:r0 + rows].contiguous(), out_dtype=torch.float32, kernel="stream")
         torch.cuda.synchronize()
-        assert torch.equal(y[r0:r0 + 16], ys), r0
+        assert torch.equal(y[r0:r0 + rows], ys), r0
+
+
+@pytest.mark.parametrize("n", [5120, 10240])
+@pytest.mark.parametrize("tn,tk", TILES)
+@pytest.mark.parametrize("m", [1, 16, 24, 64, 128])
+def test_stream_w_blocks_match_oracle(P, n, tn, tk, m):
+    """Wide weights stream 2 (5120 rows) or 4 (10240 rows) 16-row W blocks per workgroup, every
+    block meeting each X copy: every tile size (a 4-block group fills a 64-row tile), decode and
+    batched m, all-dense, mixed and all-2:4 weights, K of 6 chunks (fewer than the waves)."""
+    for frac in (0.0, 0.5, 1.0):
+        prob = I.make_problem("sw", m, n, 384, tn, tk, frac=frac, cfg=98 + m)
+        pw = pack_problem(P, prob)
+        x = dev_u16(prob.x)
+        y32 = pw.gemm(x, out_dtype=torch.float32, kernel="stream")
+        y16 = pw.gemm(x, out_dtype=torch.bfloat16, kernel="stream")
+        torch.cuda.synchronize()
+        ref = O.gemm_ref(prob.x, O.masked_weight(prob.w, prob.mask))
+        assert O.rel_error(y_host(y32), ref) <= 1e-4, frac
+        assert torch.equal(y16, y32.to(torch.bfloat16)), frac
+        if m <= 16:
+            ya = pw.gemm(x, out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            assert torch.equal(ya, y32), frac
 
 
 def test_stream_rejects_more_than_128_rows(P):
@@ -382,11 +408,13 @@ def test_stream_rejects_more_than_128_rows(P):
     assert e.value.status_name == "PATCH_E_INVALID_ARG"
 
 
-@pytest.mark.parametrize("n,k,m,want", [(1024, 8192, 64, "stream"), (16384, 1024, 128, "tiled")])
+@pytest.mark.parametrize("n,k,m,want", [(1024, 8192, 64, "stream"), (16384, 1024, 128, "tiled"),
+                                        (10240, 2048, 32, "stream")])
 def test_auto_kernel_for_small_batches(P, n, k, m, want):
     """Between 17 and 128 rows AUTO estimates both kernels: a narrow weight with a long K streams
     (the tiled kernel would give it 8 workgroups of 128 K steps), a wide one with a short K stays
-    tiled (streaming would copy all of X for each of its 1024 row blocks)."""
+    tiled at 128 rows (streaming would copy all 128 rows of X for each of its 256 workgroups), and
+    streams at 32 rows with 4 W blocks per workgroup."""
     prob = I.make_problem("am", m, n, k, 128, 128, frac=0.9, cfg=97)
     pw = pack_problem(P, prob)
     x = dev_u16(prob.x)

@@ -43,6 +43,8 @@ def case(i):
     pad_x = 8 * int(rng.integers(0, 3))
     pad_y = 8 * int(rng.integers(0, 3))
     f32 = bool(rng.integers(2))
+    if rng.random() < 0.25:  # a wide weight: 2 or 4 W blocks per streaming workgroup
+        n = tn * int(rng.integers(5120 // tn, 12288 // tn + 1))
     return dict(tn=tn, tk=tk, n=n, k=k, m=m, frac=frac, pad_x=pad_x, pad_y=pad_y, f32=f32)
 
 
