@@ -74,13 +74,14 @@ typedef enum { PATCH_TILE_DENSE = 0, PATCH_TILE_SPARSE24 = 1 } patch_tile_type;
 
 /* Kernel selection for patch_gemm_kernel.  AUTO picks STREAM for M <= 16 and
  * TILED for M > PATCH_STREAM_MAX_M; in between it estimates both kernels' time
- * from the weight's shape and packed bytes and picks STREAM only if it is
- * estimated at least 10% faster.  Forcing one is for tests and measurements. */
+ * from the weight's shape and packed bytes and picks the faster.  Forcing one
+ * is for tests and measurements. */
 typedef enum {
   PATCH_KERNEL_AUTO = 0,
   PATCH_KERNEL_TILED = 1,  /* LDS-staged MFMA tiles, for prefill-sized M */
-  PATCH_KERNEL_STREAM = 2  /* weight streaming, one workgroup per 16 rows of W, each W chunk applied
-                              to all M rows: decode and batches up to PATCH_STREAM_MAX_M rows */
+  PATCH_KERNEL_STREAM = 2  /* weight streaming, one workgroup per 16, 32 or 64 rows of W (wider
+                              weights take more), each W chunk applied to all M rows: decode and
+                              batches up to PATCH_STREAM_MAX_M rows */
 } patch_kernel;
 
 typedef struct patch_weight patch_weight; /* opaque, owned by the library */
@@ -171,8 +172,10 @@ patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t
  * inputs (the card's model is LLaMA-3.2-1B: q, k, v, o, gate, up and down
  * projections per layer, each with its own PATCH mask).  Each item is the
  * patch_gemm of its own handle, X and Y.  Items that run on the STREAM kernel
- * (as their solo patch_gemm would) share one launch of it (items with m > 64
- * one launch of their own); TILED items that fill the GPU on their own (at least
+ * (as their solo patch_gemm would) share a launch of it with the items that
+ * split K among as many waves and carry as many W blocks per workgroup (both
+ * set by the item's own m and n), so each item's Y equals its solo result;
+ * TILED items that fill the GPU on their own (at least
  * one 256 x 256 output block per compute unit) get a launch each, and the
  * other TILED items share one launch, so small projections share the chip
  * instead of running one after another; an item with K = 0 gets a zero fill.
