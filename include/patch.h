@@ -166,6 +166,36 @@ patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t
                                patch_kernel kernel, int32_t variant, void* stream);
 
 /*
+ * patch_gemm_with_workspace -- patch_gemm that may split K across workgroups.
+ *
+ * The same product as patch_gemm (card "How to use": Y = X . W_masked^T).
+ * When AUTO runs it on the streaming kernel (m <= PATCH_STREAM_MAX_M) and the
+ * weight is narrow with a long K (fewer than 5120 rows of W, at least 2048,
+ * and below 4096 for m <= 16; K >= 8192), four workgroups share each block of
+ * W rows, each taking a quarter of K: they write fp32 partial sums into the
+ * workspace, and a second launch adds the four in a fixed order into Y.
+ * Otherwise it is patch_gemm.
+ *
+ *   workspace        device, 16-byte aligned, workspace_bytes long, or NULL.
+ *                    Scratch: its contents are not kept.  The product is split
+ *                    only if workspace_bytes >= patch_gemm_workspace_size.
+ *   other arguments  as for patch_gemm.
+ *
+ * Never allocates and never blocks the host.  Calls that share a workspace
+ * must not overlap (order them on one stream).  Y is deterministic; a split
+ * product's Y sums K in another order than patch_gemm's, so the two may
+ * differ in the last bits (both are within the same error bound).
+ */
+patch_status patch_gemm_with_workspace(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx,
+                                       void* y, int64_t ldy, patch_out_dtype y_dtype, void* workspace,
+                                       int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace with which patch_gemm_with_workspace splits the product
+ * of m rows on w (0: it would not split).  *bytes is written on success;
+ * PATCH_E_INVALID_ARG for a NULL handle or pointer, or m < 0. */
+patch_status patch_gemm_workspace_size(const patch_weight* w, int64_t m, int64_t* bytes);
+
+/*
  * patch_gemm_grouped -- several independent linear layers in one launch.
  *
  * A transformer layer applies several linears to the same or to different

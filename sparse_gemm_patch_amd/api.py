@@ -24,7 +24,7 @@ DENSE, SPARSE24 = 0, 1
 
 # Exported entry points; kept in step with include/patch.h.
 SYMBOLS = ("patch_pack", "patch_gemm", "patch_gemm_kernel", "patch_gemm_grouped", "patch_gemm_grouped_kernel",
-           "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_import",
+           "patch_gemm_with_workspace", "patch_gemm_workspace_size", "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_import",
            "patch_sample_mask", "patch_pack_noalloc", "patch_destroy", "patch_last_error")
 MAX_GROUP = 16
 
@@ -81,6 +81,8 @@ def load() -> ctypes.CDLL:
     L.patch_gemm.argtypes = [vp, vp, i64, i64, vp, i64, ctypes.c_int, vp]
     L.patch_gemm_kernel.argtypes = [vp, vp, i64, i64, vp, i64, ctypes.c_int, ctypes.c_int, i32, vp]
     L.patch_gemm_grouped.argtypes = [ctypes.POINTER(GemmItem), i32, ctypes.c_int, vp]
+    L.patch_gemm_with_workspace.argtypes = [vp, vp, i64, i64, vp, i64, ctypes.c_int, vp, i64, vp]
+    L.patch_gemm_workspace_size.argtypes = [vp, i64, ctypes.POINTER(i64)]
     L.patch_gemm_grouped_kernel.argtypes = [ctypes.POINTER(GemmItem), i32, ctypes.c_int, ctypes.c_int, i32, vp]
     L.patch_unpack.argtypes = [vp, vp, i64, vp]
     L.patch_mask_unpack.argtypes = [vp, i64, ctypes.c_int, vp, vp]
@@ -95,7 +97,7 @@ def load() -> ctypes.CDLL:
     L.patch_last_error.argtypes = []
     L.patch_last_error.restype = ctypes.c_char_p
     for name in ("patch_pack", "patch_gemm", "patch_gemm_kernel", "patch_gemm_grouped", "patch_gemm_grouped_kernel",
-                 "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_import",
+                 "patch_gemm_with_workspace", "patch_gemm_workspace_size", "patch_unpack", "patch_mask_unpack", "patch_get_info", "patch_export", "patch_import",
                  "patch_sample_mask", "patch_pack_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
@@ -158,13 +160,36 @@ class PackedWeight:
                 raise ValueError(f"out must be [{m}][{self.n}]")
         return m, ldx, out, _row_major_2d(out, "out")
 
+    def workspace_size(self, m: int) -> int:
+        """Bytes of workspace with which gemm(..., workspace=...) splits K for m rows (0: no split)."""
+        n = ctypes.c_int64(0)
+        st = load().patch_gemm_workspace_size(self._h, int(m), ctypes.byref(n))
+        if st:
+            _raise(st)
+        return n.value
+
     def gemm(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
-             kernel: str = "auto", block_m: int = 0, stream=None) -> torch.Tensor:
+             kernel: str = "auto", block_m: int = 0, stream=None,
+             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
         """Y = X . W_masked^T for X bf16 [m][k]; returns Y [m][n] (bf16 or fp32).
 
         kernel "tiled" takes block_m (X rows per workgroup: 256, 192, 128 or 64; 0 =
-        the library's choice)."""
+        the library's choice).  A workspace (a device tensor, kernel "auto" only) goes
+        to patch_gemm_with_workspace, which splits K when it holds workspace_size(m)
+        bytes."""
         m, ldx, out, ldy = self._operands(x, out, out_dtype)
+        if workspace is not None:
+            if kernel != "auto":
+                raise ValueError("a workspace is taken with kernel='auto' only")
+            if not workspace.is_cuda or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous device tensor")
+            st = load().patch_gemm_with_workspace(self._h, ctypes.c_void_p(x.data_ptr()), m, ldx,
+                                                  ctypes.c_void_p(out.data_ptr()), ldy, OUT_DTYPE[out_dtype],
+                                                  ctypes.c_void_p(workspace.data_ptr()),
+                                                  workspace.numel() * workspace.element_size(), _stream_handle(stream))
+            if st:
+                _raise(st)
+            return out
         st = load().patch_gemm_kernel(self._h, ctypes.c_void_p(x.data_ptr()), m, ldx, ctypes.c_void_p(out.data_ptr()),
                                       ldy, OUT_DTYPE[out_dtype], KERNEL[kernel],
                                       int(block_m if kernel == "tiled" else 0),

@@ -377,8 +377,18 @@ static patch_status check_product(const patch_weight* w, const uint16_t* x, int6
 // Runs up to PATCH_MAX_GROUP products: those with K = 0 get a zero fill, the
 // rest one launch of the streaming kernel (m <= 16) and/or one of the tiled
 // kernel.  kernel / variant as in patch_gemm_kernel.
+// Bytes of fp32 partials a split of the product of m rows on w needs (0: no split).
+static int64_t split_bytes(const patch_weight* w, int64_t m) {
+  if (m < 1 || m > PATCH_STREAM_MAX_M || w->k == 0 || w->n == 0 || !stream_wins(w, m)) return 0;
+  const int split = stream_k_split(m, w->n, w->k);
+  return split > 1 ? (int64_t)split * m * w->n * 4 : 0;
+}
+
+// `workspace` (one product only, AUTO): when it holds split_bytes, a streamed
+// product splits its K (launch_stream_split).
 static patch_status gemm_group_common(const patch_gemm_item* items, int32_t count, int y_dtype, int kernel,
-                                      int32_t variant, void* stream) {
+                                      int32_t variant, void* stream, void* workspace = nullptr,
+                                      int64_t workspace_bytes = 0) {
   if (count < 0 || count > PATCH_MAX_GROUP)
     return fail(PATCH_E_INVALID_ARG, "group of %d products, must be 0..%d", (int)count, PATCH_MAX_GROUP);
   if (count > 0 && !items) return fail(PATCH_E_INVALID_ARG, "items is NULL");
@@ -424,6 +434,15 @@ static patch_status gemm_group_common(const patch_gemm_item* items, int32_t coun
       continue;
     }
     const bool st = kernel == PATCH_KERNEL_STREAM || (kernel == PATCH_KERNEL_AUTO && stream_wins(it.w, it.m));
+    const int64_t need = workspace && kernel == PATCH_KERNEL_AUTO ? split_bytes(it.w, it.m) : 0;
+    if (st && need > 0 && workspace_bytes >= need) {
+      gemm_problem p = make_problem(it.w, it.x, it.m, it.ldx, it.y, it.ldy);
+      p.ksplit = stream_k_split(it.m, it.w->n, it.w->k);
+      p.part = static_cast<float*>(workspace);
+      e = launch_stream_split(p, f32, s);
+      if (e != hipSuccess) return hip_fail(e, "gemm launch (streaming kernel, split K)");
+      continue;
+    }
     gemm_group& g = st ? streamed : tiled;
     g.p[g.count++] = make_problem(it.w, it.x, it.m, it.ldx, it.y, it.ldy);
   }
@@ -473,6 +492,23 @@ patch_status patch_gemm_kernel(const patch_weight* w, const uint16_t* x, int64_t
                                void* stream) {
   const patch_gemm_item it = {w, x, m, ldx, y, ldy};
   return gemm_group_common(&it, 1, enum_value(y_dtype), enum_value(kernel), variant, stream);
+}
+
+patch_status patch_gemm_with_workspace(const patch_weight* w, const uint16_t* x, int64_t m, int64_t ldx, void* y,
+                                       int64_t ldy, patch_out_dtype y_dtype, void* workspace, int64_t workspace_bytes,
+                                       void* stream) {
+  if (workspace && !aligned16(workspace)) return fail(PATCH_E_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (workspace_bytes < 0) return fail(PATCH_E_INVALID_ARG, "workspace_bytes %lld < 0", (long long)workspace_bytes);
+  const patch_gemm_item it = {w, x, m, ldx, y, ldy};
+  return gemm_group_common(&it, 1, enum_value(y_dtype), PATCH_KERNEL_AUTO, 0, stream, workspace, workspace_bytes);
+}
+
+patch_status patch_gemm_workspace_size(const patch_weight* w, int64_t m, int64_t* bytes) {
+  if (!w) return fail(PATCH_E_INVALID_ARG, "weight handle is NULL");
+  if (!bytes) return fail(PATCH_E_INVALID_ARG, "bytes is NULL");
+  if (m < 0) return fail(PATCH_E_INVALID_ARG, "m = %lld < 0", (long long)m);
+  *bytes = split_bytes(w, m);
+  return ok();
 }
 
 patch_status patch_gemm_grouped(const patch_gemm_item* items, int32_t count, patch_out_dtype y_dtype,

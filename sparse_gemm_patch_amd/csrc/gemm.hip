@@ -144,9 +144,10 @@ __device__ __forceinline__ int find_problem(const gemm_group& g, int bid, int& l
   return -1;
 }
 
-template <bool F32, int MB, int NBLK, int WAVES, int BATCH>
+template <bool F32, int MB, int NBLK, int WAVES, int BATCH, int SPLIT>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_stream(const gemm_group g) {
   static_assert(MB >= 1 && MB <= 8, "X blocks per wave");
+  static_assert(SPLIT == 1 || SPLIT == 2 || SPLIT == 4, "workgroups per W block's K range");
   static_assert(NBLK == 1 || NBLK == 2 || NBLK == 4, "16-row W blocks per workgroup");
   int local;
   const int pi = find_problem(g, blockIdx.x, local);
@@ -169,9 +170,18 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_stream(const gemm_group g) 
   // its L2 once; dealt round-robin, every XCD fetched them from memory.  A
   // block's NBLK 16-row blocks lie in one tile (16 NBLK divides TN), so they
   // share each chunk's tile descriptor and code group.
+  // With a K split, the SPLIT workgroups of one W block are consecutive in
+  // this order (one XCD), share s taking chunks [C s / SPLIT, C (s + 1) /
+  // SPLIT).  SPLIT is a template argument: computed at run time, this
+  // arithmetic sits before every workgroup's first descriptor load and cost
+  // the unsplit decode launches 0.1-0.5 us.
+  constexpr int LG = SPLIT == 4 ? 2 : SPLIT == 2 ? 1 : 0;
   const int nb = P.blocks, xcd = local & 7, base_b = nb >> 3, rem_b = nb & 7;
-  const int64_t n0 = (int64_t)(xcd * base_b + (xcd < rem_b ? xcd : rem_b) + (local >> 3)) * (16 * NBLK);
-  const int64_t chunks = k >> 6;
+  const int pos = xcd * base_b + (xcd < rem_b ? xcd : rem_b) + (local >> 3);
+  const int share = pos & (SPLIT - 1);
+  const int64_t n0 = (int64_t)(pos >> LG) * (16 * NBLK);
+  const int64_t first_chunk = ((k >> 6) * share) >> LG;
+  const int64_t chunks = ((k >> 6) * (share + 1)) >> LG;  // one past this workgroup's last chunk
   const int ks = tk == 128;                      // 64-wide K chunks per tile column: 1 << ks
   const int ns = tn == 128 ? 7 : 6;              // log2(TN)
   const int64_t desc_row = (n0 >> ns) * tiles_k;
@@ -207,7 +217,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_stream(const gemm_group g) 
   // This wave's chunks are c = wave + WAVES j.  Their tile descriptors arrive
   // with one load (lane j holds chunk j's), so that the operand loads of a
   // batch of chunks can be issued back to back before their MFMAs.
-  for (int64_t base = wave; base < chunks; base += (int64_t)WAVES * 64) {
+  for (int64_t base = first_chunk + wave; base < chunks; base += (int64_t)WAVES * 64) {
     const int nj = (int)min((int64_t)64, (chunks - base + WAVES - 1) / WAVES);
     const int64_t cl = base + (int64_t)WAVES * lane;
     const int32_t dl = lane < nj ? tile_desc[desc_row + (cl >> ks)] : 0;
@@ -293,7 +303,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_stream(const gemm_group g) 
       for (int w = 0; w < WAVES; ++w) v += red[w][mb][nl][o & 15];
       if (mm < m) {
         const int64_t col = n0 + 16 * b + nl;
-        if (F32) reinterpret_cast<float*>(y)[mm * ldy + col] = v;
+        if constexpr (SPLIT > 1) P.part[(share * m + mm) * P.n + col] = v;
+        else if (F32) reinterpret_cast<float*>(y)[mm * ldy + col] = v;
         else reinterpret_cast<uint16_t*>(y)[mm * ldy + col] = f32_to_bf16_rne(v);
       }
     }
@@ -1050,6 +1061,8 @@ gemm_problem make_problem(const patch_weight* w, const uint16_t* x, int64_t m, i
   p.n_begin = 0;
   p.bm = 0;
   p.mix = (float)row_cost(w, 0, w->tiles_n);
+  p.ksplit = 1;
+  p.part = nullptr;
   return p;
 }
 
@@ -1067,17 +1080,19 @@ bool log_launches() {
 }  // namespace
 
 namespace {
-template <bool F32, int MB, int NBLK, int WAVES, int BATCH>
+template <bool F32, int MB, int NBLK, int WAVES, int BATCH, int SPLIT = 1>
 hipError_t launch_stream_mb(gemm_group& g, hipStream_t s) {
   int64_t total = 0;
   for (int i = 0; i < g.count; ++i) {  // each product starts on a multiple of 8 (its XCD order)
+    if (g.p[i].ksplit != SPLIT) return hipErrorInvalidValue;
     g.p[i].block0 = (int32_t)total;
-    g.p[i].blocks = (int32_t)(g.p[i].n / (16 * NBLK));
+    g.p[i].blocks = (int32_t)(g.p[i].n / (16 * NBLK) * SPLIT);
     total += (g.p[i].blocks + 7) / 8 * 8;
   }
   if (total == 0) return hipSuccess;
   if (total > INT32_MAX) return hipErrorInvalidValue;  // block numbers are 32-bit
-  hipLaunchKernelGGL((k_gemm_stream<F32, MB, NBLK, WAVES, BATCH>), dim3((unsigned)total), dim3(64 * WAVES), 0, s, g);
+  hipLaunchKernelGGL((k_gemm_stream<F32, MB, NBLK, WAVES, BATCH, SPLIT>), dim3((unsigned)total), dim3(64 * WAVES), 0,
+                     s, g);
   return hipGetLastError();
 }
 template <bool F32>
@@ -1108,6 +1123,21 @@ hipError_t launch_stream_f(gemm_group& g, int waves, int nblk, int mb, hipStream
     default: return hipErrorInvalidValue;
   }
 }
+// The K-split instances: four workgroups per W block, 8 waves, 2 or 4 W blocks.
+template <bool F32>
+hipError_t launch_split_f(gemm_group& g, int nblk, int mb, hipStream_t s) {
+  switch (nblk * 16 + mb) {
+    case 32 + 1: return launch_stream_mb<F32, 1, 2, 8, 2, 4>(g, s);
+    case 32 + 2: return launch_stream_mb<F32, 2, 2, 8, 1, 4>(g, s);
+    case 32 + 4: return launch_stream_mb<F32, 4, 2, 8, 1, 4>(g, s);
+    case 32 + 8: return launch_stream_mb<F32, 8, 2, 8, 1, 4>(g, s);
+    case 64 + 1: return launch_stream_mb<F32, 1, 4, 8, 1, 4>(g, s);
+    case 64 + 2: return launch_stream_mb<F32, 2, 4, 8, 1, 4>(g, s);
+    case 64 + 4: return launch_stream_mb<F32, 4, 4, 8, 1, 4>(g, s);
+    case 64 + 8: return launch_stream_mb<F32, 8, 4, 8, 1, 4>(g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 }  // namespace
 
 int stream_x_blocks(int64_t m) { return m <= 16 ? 1 : m <= 32 ? 2 : m <= 64 ? 4 : m <= PATCH_STREAM_MAX_M ? 8 : 0; }
@@ -1124,6 +1154,61 @@ int stream_w_blocks(int64_t n) { return n >= 160 * 64 ? 4 : n >= 160 * 32 ? 2 : 
 // faster than 16 with four W or X blocks: half the reduction, and two
 // workgroups per CU).
 int stream_waves(int64_t m, int64_t n) { return stream_w_blocks(n) == 1 && stream_x_blocks(m) <= 2 ? 16 : 8; }
+
+// A narrow W (fewer than 5120 rows: one W block per workgroup, at most 319
+// workgroups) with a long K (at least 128 chunks) leaves each wave a long
+// chain of dependent chunks, and every workgroup copies all of X.  Given a
+// workspace, four workgroups share each W block's K range instead, each with
+// 4 W blocks (4096 rows and more) or 2: the X copies fall by that factor and
+// the grid stays at 256-384 workgroups.  Measured on MI355X with the weights
+// read from HBM, the summing launch included: 2048 x 8192 at m = 64 and 128
+// in 14.6 and 20.4 us against 21.6 and 36.1; 4096 x 11008 in 23.0 and 33.5
+// against 30.5 and 48.5.  At decode sizes (m <= 16) the summing launch costs
+// about what the split saves once the unsplit grid already has a workgroup
+// per CU (4096 x 11008 at m = 1: 15.1 against 13.2 us), so there only
+// narrower weights split (2048 x 8192 at m = 16: 10.5 against 11.8 us).
+// Products with 64 chunks (K = 4096) gained at most 6% before the sum.
+int stream_k_split(int64_t m, int64_t n, int64_t k) {
+  if (stream_w_blocks(n) != 1 || n < 2048 || (k >> 6) < 128) return 1;
+  return m <= 16 && n >= 4096 ? 1 : 4;
+}
+int stream_split_w_blocks(int64_t n) { return n >= 4096 ? 4 : 2; }
+
+namespace {
+// Sums the K shares' partials of a split product in share order and writes Y:
+// four columns per thread.
+template <bool F32>
+__global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ part, int split, int64_t m, int64_t n,
+                                                   void* __restrict__ y, int64_t ldy) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x, quads = n >> 2;
+  if (q >= m * quads) return;
+  const int64_t row = q / quads, col = (q - row * quads) * 4;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(part + row * n + col);
+  for (int s = 1; s < split; ++s) acc += *reinterpret_cast<const f32x4*>(part + (s * m + row) * n + col);
+  if (F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(y) + row * ldy + col) = acc;
+  } else {
+    const uint32_t lo = f32_to_bf16_rne(acc[0]) | (uint32_t)f32_to_bf16_rne(acc[1]) << 16;
+    const uint32_t hi = f32_to_bf16_rne(acc[2]) | (uint32_t)f32_to_bf16_rne(acc[3]) << 16;
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + row * ldy + col) = make_uint2(lo, hi);
+  }
+}
+}  // namespace
+
+hipError_t launch_stream_split(const gemm_problem& p, int out_f32, hipStream_t s) {
+  if (p.ksplit != 4 || !p.part || p.n % 64 || p.m < 1 || p.m > PATCH_STREAM_MAX_M) return hipErrorInvalidValue;
+  gemm_group g = {};
+  g.p[g.count++] = p;
+  const int nblk = stream_split_w_blocks(p.n), mb = stream_x_blocks(p.m);
+  if (log_launches())
+    fprintf(stderr, "patch: k_gemm_stream waves 8 w_blocks %d x_blocks %d k_split %d\n", nblk, mb, p.ksplit);
+  hipError_t e = out_f32 ? launch_split_f<true>(g, nblk, mb, s) : launch_split_f<false>(g, nblk, mb, s);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)((p.m * (p.n >> 2) + 255) / 256);
+  if (out_f32) hipLaunchKernelGGL(k_split_sum<true>, dim3(grid), dim3(256), 0, s, p.part, p.ksplit, p.m, p.n, p.y, p.ldy);
+  else hipLaunchKernelGGL(k_split_sum<false>, dim3(grid), dim3(256), 0, s, p.part, p.ksplit, p.m, p.n, p.y, p.ldy);
+  return hipGetLastError();
+}
 
 // A product's Y depends only on how many waves split its K (each wave sums its
 // chunks in order, then the waves are summed in order), not on how many X or W

@@ -91,6 +91,8 @@ struct gemm_problem {
   int64_t n_begin; // this entry covers W rows / Y columns n_begin .. n - 1
   int32_t bm;      // tiled kernels: X rows per block of this entry (set by the launcher)
   float mix;       // mean relative step cost of the entry's W rows (host scheduling only)
+  int32_t ksplit;  // streaming kernel: workgroups that share each W block's K range (1: no split, or 4)
+  float* part;     // ksplit > 1: fp32 partial sums [ksplit][m][n], one per share of K
 };
 struct gemm_group {
   int32_t count;
@@ -106,6 +108,14 @@ int stream_x_blocks(int64_t m);
 int stream_w_blocks(int64_t n);
 // Waves that split K in the streaming kernel for an m x n product (16 or 8).
 int stream_waves(int64_t m, int64_t n);
+// Workgroups that share one W block's K range of an m x n x k product when
+// the caller gives a workspace (1: it runs unsplit; else 4), and the W blocks
+// per workgroup then.
+int stream_k_split(int64_t m, int64_t n, int64_t k);
+int stream_split_w_blocks(int64_t n);
+// One product on the streaming kernel with its K split p.ksplit ways: fp32
+// partials into p.part, then a second launch that sums them in order into Y.
+hipError_t launch_stream_split(const gemm_problem& p, int out_f32, hipStream_t s);
 // One launch of the streaming kernel (every m <= PATCH_STREAM_MAX_M) / the
 // tiled kernel over a group.  block_m > 0 forces the tiled block height (256,
 // 192, 128, 64).

@@ -211,3 +211,18 @@ def test_pack_noalloc_argument_errors(lib):
     assert b"2^31" in lib.patch_last_error()
     assert call(w=0) == 1
     assert call(w=(1 << 20) + 2) == 1
+
+
+def test_workspace_argument_errors(lib):
+    """Rejected before any HIP call."""
+    vp = ctypes.c_void_p
+    n = ctypes.c_int64(-1)
+    assert lib.patch_gemm_workspace_size(None, 16, ctypes.byref(n)) == 1                 # NULL handle
+    assert lib.patch_gemm_workspace_size(vp(1 << 20), 16, None) == 1                     # NULL result
+    assert lib.patch_gemm_workspace_size(vp(1 << 20), -1, ctypes.byref(n)) == 1          # m < 0
+    assert lib.patch_gemm_with_workspace(None, None, 1, 64, None, 64, 0, None, 0, None) == 1
+    assert lib.patch_gemm_with_workspace(vp(1 << 20), vp(1 << 20), 1, 64, vp(1 << 20), 64, 0,
+                                         vp((1 << 20) + 4), 1 << 16, None) == 1           # misaligned workspace
+    assert b"16-byte" in lib.patch_last_error()
+    assert lib.patch_gemm_with_workspace(vp(1 << 20), vp(1 << 20), 1, 64, vp(1 << 20), 64, 0,
+                                         vp(1 << 20), -8, None) == 1                      # negative size
