@@ -63,6 +63,11 @@ def test_decode_workload_line():
     assert d["cpu_baseline"] is None and d["weight_copies"] >= 2
     assert sorted(d["other_m"]) == ["M=1", "M=128", "M=32", "M=64", "M=8"]
     assert all(v["dense_eq_tflops"] > 0 for v in d["other_m"].values())
+    # every decode batch size at every sparsity: 3 shapes x 3 M x 3 sparsities
+    g = d["decode_grid"]
+    assert sorted(g) == ["M=1", "M=16", "M=8"]
+    assert all(len(row) == 3 and all(v["dense_eq_tflops"] > 0 for v in row.values()) for row in g.values())
+    assert g["M=16"] and sorted(g["M=16"]) == sorted(d["sweep"])
 
 
 @pytest.mark.parametrize("wl", ["llama7b-model-prefill", "llama7b-model-decode"])
