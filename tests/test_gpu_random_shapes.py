@@ -4,7 +4,9 @@ random sparsity and output type, the library's own kernel choice and a forced on
 Each case checks the packed format bit for bit against the oracle, Y against the
 fp64 oracle (all rows up to 300, 64 sampled rows above), bf16 Y against fp32 Y
 rounded to nearest even, and, for prefill-sized M, bitwise equality of Y across
-block heights (every kernel accumulates K in the same order)."""
+block heights (every kernel accumulates K in the same order), and the call with a
+workspace: against the oracle where it splits K, bitwise equal to the call
+without one where it does not."""
 import os
 
 import numpy as np
@@ -45,6 +47,10 @@ def case(i):
     f32 = bool(rng.integers(2))
     if rng.random() < 0.25:  # a wide weight: 2 or 4 W blocks per streaming workgroup
         n = tn * int(rng.integers(5120 // tn, 12288 // tn + 1))
+    if rng.random() < 0.1:  # a narrow weight with a long K at m <= 128: the K split over a workspace
+        n = tn * int(rng.integers(2048 // tn, 5119 // tn + 1))
+        k = tk * int(rng.integers(8192 // tk, 12288 // tk + 1))
+        m = int(rng.integers(1, 129))
     return dict(tn=tn, tk=tk, n=n, k=k, m=m, frac=frac, pad_x=pad_x, pad_y=pad_y, f32=f32)
 
 
@@ -97,3 +103,13 @@ def test_random_shape(P, i):
         assert torch.equal(yt, y32)
     else:
         assert torch.equal(ys_, y32) or torch.equal(yt, y32)
+
+    # with a workspace (filled with NaN: stale contents must not matter) the library may split K
+    need = pw.workspace_size(c["m"])
+    ws = torch.full((need // 4 + 4,), float("nan"), dtype=torch.float32, device="cuda")
+    yw = pw.gemm(x, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    if need == 0:
+        assert torch.equal(yw, y32)  # nothing to split: the launch without a workspace
+    else:
+        assert O.rel_error(yw.cpu().numpy().astype(np.float64)[rows], ref) <= 1e-4
